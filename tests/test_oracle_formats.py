@@ -1,0 +1,196 @@
+"""Pins of the oracle's block decoders against hand-built blocks, the IEEE
+binary16 definition (via numpy) and the byte sizes the pages print."""
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _f16_bytes(v: float) -> bytes:
+    return np.array([v], dtype=np.float16).tobytes()
+
+
+def test_fp16_all_bit_patterns_match_numpy():
+    bits = np.arange(65536, dtype=np.uint16)
+    ref = bits.view(np.float16).astype(np.float64)
+    got = np.array([oracle.fp16_to_f64(int(b)) for b in bits])
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], ref[~nan])
+    # signed zeros keep their sign
+    assert np.signbit(got[0x8000]) and not np.signbit(got[0])
+
+
+def test_golden_sizes():
+    with open(os.path.join(GOLDEN, "sizes.txt")) as f:
+        rows = [ln.split() for ln in f if ln.strip() and not ln.startswith("#")]
+    assert rows
+    for kind, fmt, r, c, count, value in rows:
+        r, c, count = int(r), int(c), int(count)
+        nbytes = r * oracle.row_bytes(fmt, c) * count
+        if kind == "block":
+            assert nbytes == int(value)
+        else:
+            # the pages print MiB rounded half up to two decimals
+            assert abs(nbytes / 2**20 - float(value)) <= 0.005 + 1e-12
+
+
+# ---------------------------------------------------------------- Q4_0
+def q4_0_block(d: float, qs16: list[int]) -> np.ndarray:
+    return np.frombuffer(_f16_bytes(d) + bytes(qs16), dtype=np.uint8)
+
+
+@pytest.mark.parametrize("q,expect", [(8, 0.0), (0, -8.0), (15, 7.0), (9, 1.0), (7, -1.0)])
+def test_q4_0_code_offset(q, expect):
+    blk = q4_0_block(0.5, [q | (q << 4)] * 16)
+    w = oracle.dequant_row("q4_0", blk, 32)
+    assert np.all(w == expect * 0.5)
+
+
+def test_q4_0_element_order():
+    # byte j: low nibble -> element j, high nibble -> element j + 16
+    qs = [j | ((15 - j) << 4) for j in range(16)]
+    w = oracle.dequant_row("q4_0", q4_0_block(1.0, qs), 32)
+    expect = [j - 8 for j in range(16)] + [(15 - j) - 8 for j in range(16)]
+    assert w.tolist() == [float(e) for e in expect]
+
+
+@pytest.mark.parametrize("dbits", [0x0000, 0x8000, 0x0001, 0x03FF, 0x0400, 0x3C00, 0x7BFF, 0xBC00])
+def test_q4_0_scale_values(dbits):
+    # zero, negative zero, smallest subnormal, largest subnormal, smallest
+    # normal, 1, 65504, -1: every scale decodes exactly
+    d = float(np.array([dbits], dtype=np.uint16).view(np.float16)[0])
+    blk = np.frombuffer(np.array([dbits], dtype=np.uint16).tobytes() + bytes([0x0F] * 16), dtype=np.uint8)
+    w = oracle.dequant_row("q4_0", blk, 32)
+    assert w[0] == 7.0 * d and w[16] == -8.0 * d
+
+
+def test_q4_0_multi_block_row():
+    b0 = q4_0_block(2.0, [0x88] * 16)         # all zero weights
+    b1 = q4_0_block(-0.25, [0xF0] * 16)       # low 0 -> -8, high 15 -> 7
+    row = np.concatenate([b0, b1])
+    w = oracle.dequant_row("q4_0", row, 64)
+    assert np.all(w[:32] == 0.0)
+    assert np.all(w[32:48] == -8 * -0.25) and np.all(w[48:] == 7 * -0.25)
+
+
+# ---------------------------------------------------------------- Q8_0
+def test_q8_0_values_and_order():
+    q = [-128, 127, 0, 1, -1] + list(range(-50, -23))
+    blk = np.frombuffer(_f16_bytes(0.25) + np.array(q, dtype=np.int8).tobytes(), dtype=np.uint8)
+    w = oracle.dequant_row("q8_0", blk, 32)
+    assert w.tolist() == [v * 0.25 for v in q]
+
+
+def test_q8_0_block_size():
+    assert oracle.row_bytes("q8_0", 32) == 34
+    assert oracle.row_bytes("q8_0", 5376) == 5712
+    assert oracle.row_bytes("q8_0", 33) == -1
+
+
+# ---------------------------------------------------------------- Q4_K
+def pack_bits_6(sc, mn) -> bytes:
+    """Place eight 6-bit scales and eight 6-bit mins into 12 bytes, written
+    as explicit bit placement: bytes 0-3 carry scales 0-3 in bits 0-5 and
+    bits 4-5 of scales 4-7 in bits 6-7; bytes 4-7 the same for the mins;
+    bytes 8-11 carry bits 0-3 of scales 4-7 (low nibble) and of mins 4-7
+    (high nibble)."""
+    out = [0] * 12
+    for j in range(8):
+        s, m = sc[j], mn[j]
+        if j < 4:
+            out[j] |= s
+            out[j + 4] |= m
+        else:
+            out[j - 4] |= ((s >> 4) & 3) << 6
+            out[j] |= ((m >> 4) & 3) << 6
+            out[j + 4] |= (s & 15) | ((m & 15) << 4)
+    return bytes(out)
+
+
+def test_q4_k_scale_unpack_roundtrip():
+    rng = np.random.default_rng(7)
+    for _ in range(200):
+        sc = rng.integers(0, 64, 8).tolist()
+        mn = rng.integers(0, 64, 8).tolist()
+        P = np.frombuffer(pack_bits_6(sc, mn), dtype=np.uint8)
+        for j in range(8):
+            assert oracle.q4_k_scale_min(P, j) == (sc[j], mn[j])
+
+
+def q4_k_block(d, dmin, sc, mn, q256) -> np.ndarray:
+    codes = bytearray(128)
+    for c in range(4):
+        for l in range(32):
+            codes[32 * c + l] = (q256[64 * c + l] & 15) | ((q256[64 * c + 32 + l] & 15) << 4)
+    raw = _f16_bytes(d) + _f16_bytes(dmin) + pack_bits_6(sc, mn) + bytes(codes)
+    assert len(raw) == 144
+    return np.frombuffer(raw, dtype=np.uint8)
+
+
+@pytest.mark.parametrize("j", range(8))
+def test_q4_k_single_scale(j):
+    sc = [0] * 8
+    sc[j] = 1
+    q = [e % 16 for e in range(256)]
+    w = oracle.dequant_row("q4_k", q4_k_block(1.0, 0.0, sc, [0] * 8, q), 256)
+    expect = np.zeros(256)
+    expect[32 * j:32 * j + 32] = q[32 * j:32 * j + 32]
+    assert np.array_equal(w, expect)
+
+
+@pytest.mark.parametrize("j", range(8))
+def test_q4_k_single_min(j):
+    mn = [0] * 8
+    mn[j] = 63
+    w = oracle.dequant_row("q4_k", q4_k_block(0.0, 0.5, [0] * 8, mn, [5] * 256), 256)
+    expect = np.zeros(256)
+    expect[32 * j:32 * j + 32] = -0.5 * 63
+    assert np.array_equal(w, expect)
+
+
+def test_q4_k_combined_formula():
+    rng = np.random.default_rng(3)
+    sc = rng.integers(0, 64, 8).tolist()
+    mn = rng.integers(0, 64, 8).tolist()
+    q = rng.integers(0, 16, 256).tolist()
+    d, dmin = 0.013, 0.007
+    blk = q4_k_block(d, dmin, sc, mn, q)
+    w = oracle.dequant_row("q4_k", blk, 256)
+    d16 = float(np.float16(d))
+    m16 = float(np.float16(dmin))
+    for e in range(256):
+        j = e // 32
+        assert w[e] == d16 * sc[j] * q[e] - m16 * mn[j]
+
+
+def test_q4_k_requires_whole_superblocks():
+    assert oracle.row_bytes("q4_k", 256) == 144
+    assert oracle.row_bytes("q4_k", 5376) == 3024
+    assert oracle.row_bytes("q4_k", 288) == -1
+
+
+def test_generator_layout_matches_decoder():
+    """The generator's packers and the oracle's decoders agree on the layout
+    (both written from the format definitions, separately)."""
+    from quantized_dequant_matrix_amd import synth
+    rng = np.random.default_rng(11)
+    q = rng.integers(0, 16, size=(3, 32), dtype=np.uint8)
+    d = np.array([0.5, -1.25, 3.0], dtype=np.float16)
+    W = synth.pack_q4_0(d, q)
+    w = oracle.dequant_row("q4_0", W, 96)
+    assert np.array_equal(w, ((q.astype(np.float64) - 8) * d.astype(np.float64)[:, None]).reshape(-1))
+    q8 = rng.integers(-127, 128, size=(2, 32), dtype=np.int8)
+    W8 = synth.pack_q8_0(np.array([0.125, 2.0], dtype=np.float16), q8)
+    w8 = oracle.dequant_row("q8_0", W8, 64)
+    assert np.array_equal(w8, (q8.astype(np.float64) * np.array([0.125, 2.0])[:, None]).reshape(-1))
+    sc = rng.integers(0, 64, size=(1, 8), dtype=np.uint8)
+    mn = rng.integers(0, 64, size=(1, 8), dtype=np.uint8)
+    qk = rng.integers(0, 16, size=(1, 256), dtype=np.uint8)
+    Wk = synth.pack_q4_k(np.array([0.5], np.float16), np.array([0.25], np.float16), sc, mn, qk)
+    ref = q4_k_block(0.5, 0.25, sc[0].tolist(), mn[0].tolist(), qk[0].tolist())
+    assert np.array_equal(Wk, ref)

@@ -1,0 +1,119 @@
+"""Pins of the oracle's matrix-vector product: exact rational brute force on
+tiny inputs, the e_i column identity, linearity and the row/M layout."""
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle
+from quantized_dequant_matrix_amd import synth
+
+
+def exact_weights(fmt: str, W: np.ndarray, N: int, K: int):
+    """Weights as exact fractions, decoded here from the byte layout with
+    Python integers (a second, independent reading of the formats)."""
+    W = W.reshape(N, -1)
+    rows = []
+    for n in range(N):
+        r = W[n].tobytes()
+        w = []
+        if fmt == "q4_0":
+            for b in range(K // 32):
+                blk = r[18 * b:18 * b + 18]
+                d = Fraction(float(np.frombuffer(blk[:2], np.float16)[0]))
+                w += [(blk[2 + j] % 16 - 8) * d for j in range(16)]
+                w += [(blk[2 + j] // 16 - 8) * d for j in range(16)]
+        elif fmt == "q8_0":
+            for b in range(K // 32):
+                blk = r[34 * b:34 * b + 34]
+                d = Fraction(float(np.frombuffer(blk[:2], np.float16)[0]))
+                w += [(v - 256 if v > 127 else v) * d for v in blk[2:]]
+        else:
+            for b in range(K // 256):
+                blk = r[144 * b:144 * b + 144]
+                d = Fraction(float(np.frombuffer(blk[0:2], np.float16)[0]))
+                dm = Fraction(float(np.frombuffer(blk[2:4], np.float16)[0]))
+                P = blk[4:16]
+                for j in range(8):
+                    if j < 4:
+                        s, m = P[j] % 64, P[j + 4] % 64
+                    else:
+                        s = P[j + 4] % 16 + (P[j - 4] // 64) * 16
+                        m = P[j + 4] // 16 + (P[j] // 64) * 16
+                    c = j // 2
+                    for l in range(32):
+                        byte = blk[16 + 32 * c + l]
+                        q = byte % 16 if j % 2 == 0 else byte // 16
+                        w.append(d * s * q - dm * m)
+        rows.append(w)
+    return rows
+
+
+@pytest.mark.parametrize("fmt,K", [("q4_0", 32), ("q4_0", 64), ("q8_0", 32), ("q8_0", 64), ("q4_k", 256)])
+def test_brute_force_exact(fmt, K):
+    N = 5
+    W, x = synth.problem(fmt, N, K, 1, seed=1000 + K)
+    y, S = oracle.qmv(fmt, W, N, K, x)
+    ew = exact_weights(fmt, W, N, K)
+    xf = [Fraction(float(v)) for v in x[0]]
+    for n in range(N):
+        exact = sum(a * b for a, b in zip(ew[n], xf))
+        sabs = sum(abs(a * b) for a, b in zip(ew[n], xf))
+        # float64 accumulation of K exactly-representable products
+        bound = K * 2.0**-53 * float(sabs)
+        assert abs(y[0, n] - float(exact)) <= bound
+        assert abs(S[0, n] - float(sabs)) <= bound
+
+
+@pytest.mark.parametrize("fmt,K", [("q4_0", 96), ("q8_0", 64), ("q4_k", 512)])
+def test_unit_vector_gives_column(fmt, K):
+    N = 7
+    W, _ = synth.problem(fmt, N, K, 1, seed=5)
+    rb = oracle.row_bytes(fmt, K)
+    for i in [0, 1, 15, 16, 17, 31, K - 1]:
+        e = np.zeros((1, K), dtype=np.float32)
+        e[0, i] = 1.0
+        y, _ = oracle.qmv(fmt, W, N, K, e)
+        col = [oracle.dequant_row(fmt, W[n * rb:(n + 1) * rb], K)[i] for n in range(N)]
+        assert y[0].tolist() == col
+
+
+def test_linearity_and_power_of_two_scaling():
+    N, K = 9, 128
+    W, _ = synth.problem("q4_0", N, K, 2, seed=77)
+    # integer-valued activations, so x[0] + x[1] is exact in float32
+    x = np.random.default_rng(77).integers(-1000, 1000, size=(2, K)).astype(np.float32)
+    y, S = oracle.qmv("q4_0", W, N, K, x, M=2)
+    y12, _ = oracle.qmv("q4_0", W, N, K, (x[0] + x[1])[None, :])
+    assert np.allclose(y12[0], y[0] + y[1], rtol=0, atol=1e-12 * (S[0] + S[1]).max())
+    y2, _ = oracle.qmv("q4_0", W, N, K, 2 * x[:1])
+    assert np.array_equal(y2[0], 2 * y[0])
+
+
+def test_rows_subset_and_batch_layout():
+    N, K, M = 11, 64, 3
+    W, x = synth.problem("q8_0", N, K, M, seed=9)
+    y, S = oracle.qmv("q8_0", W, N, K, x, M=M)
+    rows = [10, 0, 3, 3]
+    ys, Ss = oracle.qmv("q8_0", W, N, K, x, M=M, rows=rows)
+    assert np.array_equal(ys, y[:, rows]) and np.array_equal(Ss, S[:, rows])
+    for m in range(M):
+        ym, _ = oracle.qmv("q8_0", W, N, K, x[m:m + 1])
+        assert np.array_equal(ym[0], y[m])
+
+
+def test_zero_weights_give_zero():
+    # all codes 8 -> every Q4_0 weight is zero; S is zero too
+    K, N = 64, 3
+    W = np.frombuffer((np.array([1.0], np.float16).tobytes() + bytes([0x88] * 16)) * (N * K // 32), np.uint8)
+    x = np.random.default_rng(0).standard_normal((1, K)).astype(np.float32)
+    y, S = oracle.qmv("q4_0", W, N, K, x)
+    assert np.all(y == 0) and np.all(S == 0)
+
+
+def test_rejects_bad_shapes():
+    W = np.zeros(18, np.uint8)
+    with pytest.raises(ValueError):
+        oracle.qmv("q4_0", W, 1, 33, np.zeros((1, 33), np.float32))
+    with pytest.raises(ValueError):
+        oracle.qmv("q4_0", W, 1, 32, np.zeros((1, 32), np.float32), rows=[1])
