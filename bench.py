@@ -1,0 +1,283 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused-dequant quantized GEMV path on one MI355X.
+
+Workload (the headline configuration): Q4_0 weights at the dense FFN gate
+shape N=21504, K=5376, M=1 -- one plain matrix-vector product and one gated
+GELU pair over two independent matrices of that shape.  One step = both
+products over one activation vector.  Inputs are seeded synthetic data with
+the weight/activation distributions of the block formats; they are resident
+in HBM before timing starts.  Four independent slot sets (781 MB, more than
+twice the 256 MB last-level cache) are rotated so that every step streams its
+weights from HBM, as a decoder streams each layer's weights once per token.
+
+Metric: effective GB/s = algorithmic bytes (weights + activations + outputs)
+per step / time per step, and the fraction of the 8 TB/s HBM peak.
+
+Usage: python bench.py [--gpus 1] [--steps 200] [--warmup 20] [--no-rows] [--no-cpu-baseline]
+Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+HBM_PEAK_GBS = 8000.0  # MI355X published HBM3E bandwidth
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--slots", type=int, default=4)
+    p.add_argument("--no-rows", action="store_true", help="skip the per-row measurements of the other workloads")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=10.0)
+    return p.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the path has no multi-GPU part "
+              "in this build", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from quantized_dequant_matrix_amd import qmv, synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    c = synth.CONFIGS["c2"]
+    N, K = c["N"], c["K"]
+    Wg, Wu, x = synth.gate_up_problem()
+    Ws, _ = synth.config_problem("c2")  # the plain product uses the gate-shape matrix of seed c2
+    # slot sets: distinct device copies (the cache does not deduplicate)
+    S = args.slots
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    slots = [(t(Ws), t(Wg), t(Wu)) for _ in range(S)]
+    xd = t(x)
+    y1 = torch.empty((1, N), device=dev)
+    h = torch.empty((1, N), device=dev)
+    wbytes = Ws.nbytes
+    bytes_single = wbytes + K * 4 + N * 4
+    bytes_pair = 2 * wbytes + K * 4 + N * 4
+    bytes_step = bytes_single + bytes_pair
+
+    def step(i, ev=None):
+        a, g, u = slots[i % S]
+        if ev is not None:
+            ev[0].record()
+        qmv.qmv_q4_0(a, xd, y1, N, K, 1)
+        if ev is not None:
+            ev[1].record()
+        qmv.qmv_q4_0_geglu(g, u, xd, h, N, K, 1)
+        if ev is not None:
+            ev[2].record()
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    # whole-step timing
+    E0, E1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    E0.record()
+    for i in range(args.steps):
+        step(i)
+    E1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_step = E0.elapsed_time(E1) / args.steps
+
+    # per-kernel durations (events around each launch, same stream)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    for i in range(args.steps):
+        step(i, evs[i])
+    torch.cuda.synchronize()
+    t_single = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    t_pair = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+
+    value = bytes_step / (ms_step * 1e-3) / 1e9
+    kernels = {
+        "qmv_q4_0 (gemv_unit_kernel<Q4_0,2,false>)": {
+            "bytes": bytes_single, "us": t_single * 1e3,
+            "GB/s": bytes_single / (t_single * 1e-3) / 1e9},
+        "qmv_q4_0_geglu (gemv_unit_kernel<Q4_0,1,true>)": {
+            "bytes": bytes_pair, "us": t_pair * 1e3,
+            "GB/s": bytes_pair / (t_pair * 1e-3) / 1e9},
+    }
+    dom_name, dom = max(kernels.items(), key=lambda kv: kv[1]["us"])
+    roofline = {
+        "bound": "hbm",
+        "kernel": dom_name,
+        "achieved": round(dom["GB/s"], 1),
+        "peak": HBM_PEAK_GBS,
+        "unit": "GB/s",
+        "frac": round(dom["GB/s"] / HBM_PEAK_GBS, 4),
+        "traffic": None,
+    }
+
+    rows = None
+    if not args.no_rows:
+        rows = measure_rows(torch, qmv, synth, dev)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(synth, Ws, Wg, Wu, x, N, K, bytes_step, args.cpu_seconds)
+
+    out = {
+        "metric": "effective GB/s and % of HBM peak for fused-dequant Q4_0/Q8_0 GEMV, M=1",
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "q4_0 weights, f32 activations, f32 accumulation",
+        "data": "synthetic (seeded PCG64; Q4_0 d=|N(0,1)|*0.02, q~U{0..15}; x~N(0,1))",
+        "config": {
+            "workload": "Q4_0 GEMV 21504x5376 M=1 + gated GELU pair (two 21504x5376 Q4_0), one step = both",
+            "N": N, "K": K, "M": 1, "bytes_per_step": bytes_step, "slot_sets": S,
+            "working_set_MB": round(S * 3 * wbytes / 1e6, 1),
+        },
+        "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),
+        "wall_s_timed": round(wall, 4),
+        "roofline": roofline,
+        "kernels": kernels,
+        "cpu_baseline": cpu,
+        "rows": rows,
+    }
+    print(json.dumps(out))
+
+
+def _time_loop(torch, fn, iters, warm=5):
+    for i in range(warm):
+        fn(i)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(iters):
+        fn(i)
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / iters  # ms
+
+
+def measure_rows(torch, qmv, synth, dev):
+    """Effective GB/s of every other workload (context next to the headline)."""
+    res = {}
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    # C1: Q4_0 4096 x 4096, 64 slots (604 MB)
+    c = synth.CONFIGS["c1"]
+    W, x = synth.config_problem("c1")
+    Wd = t(W)
+    slots = [Wd.clone() for _ in range(64)]
+    xd, y = t(x), torch.empty((1, c["N"]), device=dev)
+    ms = _time_loop(torch, lambda i: qmv.qmv_q4_0(slots[i % 64], xd, y, c["N"], c["K"], 1), 200)
+    b = W.nbytes + c["K"] * 4 + c["N"] * 4
+    res["c1_qmv_q4_0_4096x4096"] = {"us": ms * 1e3, "bytes": b, "GB/s": b / ms / 1e6}
+    del slots, Wd
+
+    # C5: Q4_K 21504 x 5376, 8 slots
+    c = synth.CONFIGS["c5"]
+    W, x = synth.config_problem("c5")
+    slots = [t(W) for _ in range(8)]
+    xd, y = t(x), torch.empty((1, c["N"]), device=dev)
+    ms = _time_loop(torch, lambda i: qmv.qmv_q4_k(slots[i % 8], xd, y, c["N"], c["K"], 1), 100)
+    b = W.nbytes + c["K"] * 4 + c["N"] * 4
+    res["c5_qmv_q4_k_21504x5376"] = {"us": ms * 1e3, "bytes": b, "GB/s": b / ms / 1e6}
+    del slots
+
+    # C4: Q4_0 x Q8 activations, 5376 x 21504, M = 1, 16, 512; 8 slots
+    c = synth.CONFIGS["c4"]
+    N, K = c["N"], c["K"]
+    W, _ = synth.config_problem("c4", M=1)
+    slots = [t(W) for _ in range(8)]
+    for M in c["Ms"]:
+        x = synth.activations(M, K, synth.SEEDS["c4"])
+        xd, y = t(x), torch.empty((M, N), device=dev)
+        wsb = qmv.qmm_q4_0_q8act_ws_bytes(K, M)
+        ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
+        iters = 100 if M < 512 else 5
+        ms = _time_loop(torch, lambda i: qmv.qmm_q4_0_q8act(slots[i % 8], xd, y, N, K, M, ws, wsb), iters,
+                        warm=2)
+        b = W.nbytes + M * K * 4 + M * N * 4
+        res[f"c4_qmm_q4_0_q8act_M{M}"] = {"us": ms * 1e3, "bytes": b, "GB/s": b / ms / 1e6,
+                                          "int_TOPS": 2.0 * M * N * K / ms / 1e9}
+    del slots
+
+    # C3: Q8_0 262144 x 5376 + soft-cap + top-10 (1.5 GB: one copy streams)
+    c = synth.CONFIGS["c3"]
+    W, x = synth.config_problem("c3")
+    Wd, xd = t(W), t(x)
+    del W
+    k = c["k"]
+    wsb = qmv.logits_topk_ws_bytes(c["N"], 1, k)
+    ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
+    vals = torch.empty((1, k), device=dev)
+    idx = torch.empty((1, k), dtype=torch.int32, device=dev)
+    ms = _time_loop(torch, lambda i: qmv.logits_topk(Wd, xd, vals, idx, c["N"], c["K"], 1, k, c["softcap"], ws,
+                                                     wsb), 20, warm=3)
+    b = Wd.numel() + c["K"] * 4 + c["N"] * 4
+    res["c3_logits_topk_q8_0_262144x5376_k10"] = {"us": ms * 1e3, "bytes": b, "GB/s": b / ms / 1e6}
+    y = torch.empty((1, c["N"]), device=dev)
+    ms = _time_loop(torch, lambda i: qmv.qmv_q8_0(Wd, xd, y, c["N"], c["K"], 1), 20, warm=3)
+    res["c3_qmv_q8_0_only_262144x5376"] = {"us": ms * 1e3, "bytes": b, "GB/s": b / ms / 1e6}
+    for v in res.values():
+        for key in list(v):
+            if isinstance(v[key], float):
+                v[key] = round(v[key], 2)
+    return res
+
+
+def cpu_baseline(synth, Ws, Wg, Wu, x, N, K, bytes_step, seconds):
+    """The float64 oracle on the host cores, timed on whole steps of the same
+    workload (one plain product and the gated pair) until `seconds` pass."""
+    import oracle
+    reps = 0
+    t0 = time.perf_counter()
+    while True:
+        oracle.qmv("q4_0", Ws, N, K, x)
+        g, _ = oracle.qmv("q4_0", Wg, N, K, x)
+        u, _ = oracle.qmv("q4_0", Wu, N, K, x)
+        oracle.geglu(g, u)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    return {
+        "value": round(bytes_step * reps / el / 1e9, 3),
+        "unit": "GB/s",
+        "cores": oracle.num_threads(),
+        "kind": "oracle",
+        "sample": f"{reps} whole steps (3 x 21504x5376 Q4_0 matrices each) in {el:.1f} s, float64, OpenMP",
+        "cpu_model": _cpu_model(),
+    }
+
+
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,162 @@
+/*
+ * qmv.h -- C ABI of libqmv.so: matrix-vector (and small matrix-matrix)
+ * products over block-quantized weights with the dequantization fused into
+ * the dot product, for AMD Instinct MI355X (gfx950).
+ *
+ * Sources ("the pages"):
+ *   [roadmap]  "Gemma 4 M4 Max kernel roadmap" (gem, docs/research)
+ *   [captable] "Metal kernel capability table (Phase B ground truth)" (larql)
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Memory.  Every buffer pointer is a DEVICE pointer owned by the caller.  The
+ *   library allocates nothing, copies nothing between host and device and
+ *   never synchronizes; buffers may be reused across calls (the persistent
+ *   buffer path, [roadmap K2: persistent/no-copy buffers; K4: arenas
+ *   allocated once, no tensor-sized allocation during generation]).
+ *   Weights and activations are only read.  Outputs and workspaces must not
+ *   overlap any input.
+ * Weights W.  N rows, row-major, each row K weights stored as K/32 blocks
+ *   (Q4_0, Q8_0) or K/256 super-blocks (Q4_K) in the GGUF byte layout:
+ *     Q4_0 (18 B / 32 weights): fp16 d, 16 bytes of codes; byte j holds
+ *          element j (low nibble) and element j+16 (high nibble);
+ *          w = (q - 8) * d.
+ *     Q8_0 (34 B / 32 weights): fp16 d, 32 int8 codes; w = q * d.
+ *     Q4_K (144 B / 256 weights): fp16 d, fp16 dmin, 12 bytes packing eight
+ *          6-bit sub-block scales and eight 6-bit mins, 128 code bytes;
+ *          w = d * scale_j * q - dmin * min_j for sub-block j.
+ *   [captable section 1: 18 B Q4_0, 144 B Q4_K; roadmap K1: Q4_0 and Q8_0
+ *   dequantization]
+ * Activations x: float32 [M][K] row-major.  Outputs y: float32 [M][N].
+ * Accumulation is float32 [roadmap K2 step 1: F32 accumulation].
+ * Stream.  Work is enqueued on `stream` (0 = the null stream) and runs
+ *   asynchronously; QMV_OK means "enqueued".  Calls are reentrant when they
+ *   do not share output or workspace buffers.
+ * Errors.  All arguments are checked on the host before anything is
+ *   enqueued; on any error nothing is launched and the call returns the
+ *   status below [captable section 9: legal dimensions are checked at
+ *   dispatch, not assumed; a path may not silently drop work; captable
+ *   findings F6, F13 and F17 are the defects this rules out]:
+ *     QMV_ERR_NULL       a required pointer is NULL
+ *     QMV_ERR_SHAPE      N, M < 1; K < 32 or K % 32 != 0 (K % 256 != 0 for
+ *                        Q4_K); a size or a byte count overflows int64, or
+ *                        N >= 2^31
+ *     QMV_ERR_ALIGN      W or a workspace is not 16-byte aligned, or an f32
+ *                        / int32 buffer is not 4-byte aligned
+ *     QMV_ERR_WORKSPACE  workspace smaller than the *_ws_bytes() size
+ *     QMV_ERR_ARG        other argument out of range (k, softcap)
+ *     QMV_ERR_LAUNCH     the HIP runtime rejected a launch
+ *   There is no ceiling on K.  Any N is accepted (row tails are masked).
+ */
+#ifndef QMV_H
+#define QMV_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    QMV_OK = 0,
+    QMV_ERR_NULL = 1,
+    QMV_ERR_SHAPE = 2,
+    QMV_ERR_ALIGN = 3,
+    QMV_ERR_WORKSPACE = 4,
+    QMV_ERR_LAUNCH = 5,
+    QMV_ERR_ARG = 6
+} qmv_status;
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* qmv_status_str(int status);
+
+/* y[m][n] = sum_k w[n][k] * x[m][k], Q4_0 weights.
+ * [roadmap K2 step 1: direct Q4_0 matrix-vector with fused dequantization
+ *  and F32 accumulation; captable section 1: q4_f32_matvec, Q4_0 x f32]
+ * M > 1 is M independent matrix-vector products. */
+int qmv_q4_0(const void* W, const float* x, float* y,
+             int64_t N, int64_t K, int64_t M, hipStream_t stream);
+
+/* As qmv_q4_0 for Q8_0 weights.
+ * [roadmap K1: Q8_0 dequantization, matrix-vector; K2 step 6: Q8_0
+ *  embedding/output projection] */
+int qmv_q8_0(const void* W, const float* x, float* y,
+             int64_t N, int64_t K, int64_t M, hipStream_t stream);
+
+/* As qmv_q4_0 for Q4_K weights (K % 256 == 0).
+ * [captable section 1: q4k_matvec, Q4_K 144 B x f32] */
+int qmv_q4_k(const void* W, const float* x, float* y,
+             int64_t N, int64_t K, int64_t M, hipStream_t stream);
+
+/* Gated GELU projection pair: h[m][n] = gelu(g) * u with g = W_gate x[m],
+ * u = W_up x[m], both Q4_0 [N][K], gelu the tanh form
+ * v/2 (1 + tanh(sqrt(2/pi) (v + 0.044715 v^3))).  Both matrices are read
+ * in one launch.
+ * [roadmap K1: GELU-gated FFN; K2 step 5: gated GELU FFN projection pair;
+ *  captable section 4: q4k_ffn_gate_up (two matrices, one dispatch) and
+ *  geglu_gelu_tanh] */
+int qmv_q4_0_geglu(const void* W_gate, const void* W_up, const float* x, float* h,
+                   int64_t N, int64_t K, int64_t M, hipStream_t stream);
+
+/* Q4_0 weights times Q8-quantized activations, y float32 [M][N].
+ * Step 1 quantizes each 32-element block of x (float32 arithmetic):
+ *   amax = max|x|, d_x = amax / 127 (IEEE division),
+ *   q = clamp(round_half_away_from_zero(x / d_x), -127, 127),
+ *   amax == 0 -> d_x = 0 and q = 0;
+ * the int8 codes and scales go to the workspace.  Step 2 forms the exact
+ * int32 block sums isum = sum_j (q_w - 8) * q_x with integer dot products
+ * (int8 MFMA for M >= 16) and accumulates y += isum * d_w * d_x in float32.
+ * Activations must be finite.
+ * [captable section 1: q4_matvec_v4, Q4_0 x Q8 int8 + scales; section 2:
+ *  quantize_q8; roadmap K3: batched Q4_0 matrix-matrix kernels for prefill]
+ * ws: device buffer of at least qmm_q4_0_q8act_ws_bytes(K, M) bytes,
+ * 16-byte aligned, contents overwritten. */
+size_t qmm_q4_0_q8act_ws_bytes(int64_t K, int64_t M);
+int qmm_q4_0_q8act(const void* W, const float* x, float* y,
+                   int64_t N, int64_t K, int64_t M,
+                   void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Logit projection over a Q8_0 tied embedding, soft-cap and top-k.
+ *   y[m][n] = sum_k w[n][k] x[m][k]                (float32)
+ *   z = softcap * tanh(y / softcap)
+ *   top_idx[m][0..k) = indices of the k largest y[m][.], largest first,
+ *     equal values -> lower index first, NaN after all numbers;
+ *   top_val[m][i] = z[m][top_idx[m][i]].
+ * Ranking uses y: the cap is strictly increasing, so it selects the same
+ * set, and ranking after the cap would let float32 saturation near the cap
+ * decide it.  1 <= k <= min(N, 64); softcap finite and > 0.
+ * [roadmap K1: logit soft-capping; K2 step 6: Q8_0 output projection and
+ *  on-GPU top-k reduction; captable section 6: f32_topk_partial, a
+ *  two-phase partial/fan-in top-k]
+ * ws: device buffer of at least logits_topk_ws_bytes(N, M, k) bytes,
+ * 16-byte aligned, contents overwritten (it holds y). */
+size_t logits_topk_ws_bytes(int64_t N, int64_t M, int32_t k);
+int logits_topk(const void* W_q8_0, const float* x, float* top_val, int32_t* top_idx,
+                int64_t N, int64_t K, int64_t M, int32_t k, float softcap,
+                void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* ---- diagnostics: expose intermediate results of the paths above so
+ * that tests can check them bit for bit ---- */
+
+/* Step 1 of qmm_q4_0_q8act alone: q int8 [M][K], d float32 [M][K/32]. */
+int qmvdbg_quantize_q8(const float* x, int8_t* q, float* d,
+                       int64_t K, int64_t M, hipStream_t stream);
+
+/* Integer block sums of qmm_q4_0_q8act for given int8 activations, from the
+ * same kernels (same M-dependent choice): isum int32 [M][N][K/32]. */
+int qmvdbg_q4_0_q8_blocksums(const void* W, const int8_t* qx, int32_t* isum,
+                             int64_t N, int64_t K, int64_t M, hipStream_t stream);
+
+/* The top-k stages of logits_topk on a given float32 vector y [M][N]:
+ * same ordering rule, values returned as softcap * tanh(y / softcap). */
+int qmvdbg_topk_f32(const float* y, float* top_val, int32_t* top_idx,
+                    int64_t N, int64_t M, int32_t k, float softcap,
+                    void* ws, size_t ws_bytes, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QMV_H */

@@ -1,0 +1,396 @@
+// Fused-dequant matrix-vector kernels for Q4_0, Q8_0 and Q4_K weights with
+// float32 activations and float32 accumulation, and the gated GELU pair.
+//
+// What is computed: y[n] = sum_k w[n][k] x[k] with w decoded from the block
+// formats on the fly ["Gemma 4 M4 Max kernel roadmap", K2 step 1: direct
+// Q4_0 matrix-vector with fused dequantization and F32 accumulation; step 5:
+// gated GELU FFN projection pair; "Metal kernel capability table", section 1
+// (q4_f32_matvec, q4k_matvec) and section 4 (q4k_ffn_gate_up: both matrices
+// in one dispatch)].
+//
+// The pages' Metal kernels give each SIMD group four or eight rows with
+// threadgroup staging.  On gfx950 the layout is chosen for wave64 and HBM
+// instead:
+//   * A lane owns one 256-weight "unit" (8 blocks, 144 B or 272 B) of a row,
+//     streamed with 16-byte loads; every block sits at a compile-time byte
+//     offset inside the unit, so no per-lane realignment logic is needed.
+//   * The L = K/256 lanes that own the units of one row form a segment; a
+//     wave holds S = 64/L segments (3 rows at K = 5376, 4 at K = 4096), so
+//     every load instruction moves whole rows and nearly all lanes work.
+//   * The activation vector is staged once per workgroup in LDS, padded per
+//     unit so that the lanes of a segment hit different banks; each lane
+//     reuses the 32 values of a block for R rows.
+//   * Each row's partial sums are reduced across its segment with cross-lane
+//     shuffles.
+// Codes are turned into exact signed values before multiplying:
+//   Q4_0: (q - 8) * 16 as a signed byte, from (b ^ 0x88) & 0xF0, then one
+//         byte-select convert per weight; the factor 16 is folded into d.
+//   Q8_0: the signed code byte is converted directly.
+//   Q4_K: w = fma(d*scale, q, -dmin*min) per weight, exact up to one rounding.
+// So every product carries at most the rounding of float32 arithmetic on
+// the exact weight, and the float32 sums stay within 1e-5 * sum|w x|.
+#include <utility>
+
+#include "qmv_device.h"
+#include "qmv_internal.h"
+
+namespace qmv {
+namespace {
+
+template <int N, typename Fn>
+__device__ __forceinline__ void static_for(Fn&& fn) {
+    [&]<int... I>(std::integer_sequence<int, I...>) {
+        (fn(std::integral_constant<int, I>{}), ...);
+    }(std::make_integer_sequence<int, N>{});
+}
+
+// ---------------------------------------------------------------- Q4_0
+// Block k (0..7) of a 144-byte unit U[36]: fp16 d at byte 18k, codes at
+// bytes 18k+2 .. 18k+17.  Returns d/16 * sum_j 16 (q_j - 8) x_j.
+template <int k>
+__device__ __forceinline__ float q4_0_block_dot(const uint32_t* U, const float* xk) {
+    constexpr int b0 = 18 * k;
+    constexpr int dwd = b0 >> 2;
+    const uint32_t dbits = ((b0 & 3) == 2) ? (U[dwd] >> 16) : (U[dwd] & 0xffffu);
+    const float d16 = half_bits_to_float(dbits) * 0.0625f;
+    constexpr int qb = b0 + 2;
+    uint32_t qs[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        if constexpr ((qb & 3) == 0) {
+            qs[t] = U[(qb >> 2) + t];
+        } else {
+            qs[t] = shift16(U[(qb >> 2) + t + 1], U[(qb >> 2) + t]);
+        }
+    }
+    float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        const uint32_t v = qs[t] ^ 0x88888888u;
+        const uint32_t hi = v & 0xF0F0F0F0u;          // elements 16+4t+i
+        const uint32_t lo = (v << 4) & 0xF0F0F0F0u;   // elements 4t+i
+        s0 = fmaf(sbyte<0>(lo), xk[4 * t + 0], s0);
+        s1 = fmaf(sbyte<1>(lo), xk[4 * t + 1], s1);
+        s2 = fmaf(sbyte<2>(lo), xk[4 * t + 2], s2);
+        s3 = fmaf(sbyte<3>(lo), xk[4 * t + 3], s3);
+        s0 = fmaf(sbyte<0>(hi), xk[16 + 4 * t + 0], s0);
+        s1 = fmaf(sbyte<1>(hi), xk[16 + 4 * t + 1], s1);
+        s2 = fmaf(sbyte<2>(hi), xk[16 + 4 * t + 2], s2);
+        s3 = fmaf(sbyte<3>(hi), xk[16 + 4 * t + 3], s3);
+    }
+    return d16 * ((s0 + s1) + (s2 + s3));
+}
+
+// ---------------------------------------------------------------- Q8_0
+// Block k (0..7) of a 272-byte unit U[68]: fp16 d at byte 34k, int8 codes at
+// bytes 34k+2 .. 34k+33 (read in place with byte selects).
+template <int k>
+__device__ __forceinline__ float q8_0_block_dot(const uint32_t* U, const float* xk) {
+    constexpr int b0 = 34 * k;
+    constexpr int dwd = b0 >> 2;
+    const uint32_t dbits = ((b0 & 3) == 2) ? (U[dwd] >> 16) : (U[dwd] & 0xffffu);
+    const float d = half_bits_to_float(dbits);
+    float s[4] = {0.f, 0.f, 0.f, 0.f};
+    static_for<32>([&](auto ec) {
+        constexpr int e = decltype(ec)::value;
+        constexpr int pos = b0 + 2 + e;
+        s[e & 3] = fmaf(sbyte<pos & 3>(U[pos >> 2]), xk[e], s[e & 3]);
+    });
+    return d * ((s[0] + s[1]) + (s[2] + s[3]));
+}
+
+// ---------------------------------------------------------------- Q4_K
+// Sub-block j (0..7) of a 144-byte super-block U[36]: d, dmin in dword 0,
+// 6-bit scales/mins in bytes 4..15, codes of sub-blocks 2c, 2c+1 in the low
+// and high nibbles of bytes 16+32c .. 16+32c+31.
+template <int j>
+__device__ __forceinline__ float q4_k_sub_dot(const uint32_t* U, const float* xk) {
+    auto P = [&](int i) -> uint32_t { return (U[1 + (i >> 2)] >> (8 * (i & 3))) & 0xffu; };
+    uint32_t sc, mn;
+    if constexpr (j < 4) {
+        sc = P(j) & 63u;
+        mn = P(j + 4) & 63u;
+    } else {
+        sc = (P(j + 4) & 15u) | ((P(j - 4) >> 6) << 4);
+        mn = (P(j + 4) >> 4) | ((P(j) >> 6) << 4);
+    }
+    const float a = half_bits_to_float(U[0] & 0xffffu) * static_cast<float>(sc);  // exact
+    const float nb = -(half_bits_to_float(U[0] >> 16) * static_cast<float>(mn));  // exact
+    constexpr int c = j >> 1;
+    float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+        const uint32_t raw = U[4 + 8 * c + t];
+        const uint32_t q = (j & 1) ? ((raw >> 4) & 0x0F0F0F0Fu) : (raw & 0x0F0F0F0Fu);
+        s0 = fmaf(fmaf(a, ubyte<0>(q), nb), xk[4 * t + 0], s0);
+        s1 = fmaf(fmaf(a, ubyte<1>(q), nb), xk[4 * t + 1], s1);
+        s2 = fmaf(fmaf(a, ubyte<2>(q), nb), xk[4 * t + 2], s2);
+        s3 = fmaf(fmaf(a, ubyte<3>(q), nb), xk[4 * t + 3], s3);
+    }
+    return (s0 + s1) + (s2 + s3);
+}
+
+template <int F, int k>
+__device__ __forceinline__ float unit_block_dot(const uint32_t* U, const float* xk) {
+    if constexpr (F == kQ4_0) return q4_0_block_dot<k>(U, xk);
+    else if constexpr (F == kQ8_0) return q8_0_block_dot<k>(U, xk);
+    else return q4_k_sub_dot<k>(U, xk);
+}
+
+// Stage x[0..K) into LDS as G padded unit slices.
+__device__ __forceinline__ void stage_x(float* xs, const float* __restrict__ x, int G) {
+    const int n = G * kUnitElems;
+    for (int i = threadIdx.x; i < n; i += kBlockThreads) {
+        xs[(i >> 8) * kXsStride + (i & 255)] = x[i];
+    }
+}
+
+// ------------------------------------------------------------ unit kernel
+// K % 256 == 0 and G = K/256 <= 63.  Lane (segment s, unit u) of a wave
+// handles unit u of R consecutive rows per pass; a pass covers S*R rows.
+// PAIR: the same rows of two matrices (gate, up), output gelu(g) * u.
+template <int F, int R, bool PAIR>
+__global__ __launch_bounds__(kBlockThreads)
+void gemv_unit_kernel(const uint8_t* __restrict__ W0, const uint8_t* __restrict__ W1,
+                      const float* __restrict__ x, float* __restrict__ y,
+                      int N, int G, int S, int npasses) {
+    constexpr int VEC = UnitInfo<F>::kVec;
+    constexpr int UB = UnitInfo<F>::kBytes;
+    constexpr int NM = PAIR ? 2 : 1;
+    extern __shared__ float xs[];
+
+    const int lane = threadIdx.x & (kWave - 1);
+    const int L = G;
+    const int seg = lane / L;
+    const int u = lane - seg * L;
+    const bool active = seg < S;
+    const int64_t row_bytes = static_cast<int64_t>(G) * UB;
+    const int wave_stride = gridDim.x * kWavesPerBlock;
+    int pass = blockIdx.x * kWavesPerBlock + (threadIdx.x / kWave);
+
+    uint32_t U[NM * R][VEC * 4];
+    auto load = [&](int p) {
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const int row = (p * S + seg) * R + r;
+            const bool ok = active && row < N;
+#pragma unroll
+            for (int m = 0; m < NM; ++m) {
+                if (ok) {
+                    const uint8_t* base = (m == 0 ? W0 : W1) + row * row_bytes + u * UB;
+                    const uint4* src = reinterpret_cast<const uint4*>(base);
+#pragma unroll
+                    for (int t = 0; t < VEC; ++t) {
+                        const uint4 v = src[t];
+                        U[m * R + r][4 * t + 0] = v.x;
+                        U[m * R + r][4 * t + 1] = v.y;
+                        U[m * R + r][4 * t + 2] = v.z;
+                        U[m * R + r][4 * t + 3] = v.w;
+                    }
+                } else {
+#pragma unroll
+                    for (int t = 0; t < 4 * VEC; ++t) U[m * R + r][t] = 0u;
+                }
+            }
+        }
+    };
+
+    // Start the weight stream before staging the activations.
+    if (pass < npasses) load(pass);
+    stage_x(xs, x, G);
+    __syncthreads();
+
+    while (pass < npasses) {
+        // Re-derive the LDS pointer each pass so that the compiler does not
+        // hoist the whole 1 KB activation slice into registers for the
+        // lifetime of the loop (that would cap occupancy at one wave/SIMD).
+        int xoff = u * kXsStride;
+        asm volatile("" : "+v"(xoff));
+        const float* xw = xs + xoff;
+        float acc[NM * R];
+#pragma unroll
+        for (int i = 0; i < NM * R; ++i) acc[i] = 0.f;
+        static_for<8>([&](auto kc) {
+            constexpr int k = decltype(kc)::value;
+            float xk[32];
+            const float4* xv = reinterpret_cast<const float4*>(xw + 32 * k);
+#pragma unroll
+            for (int t = 0; t < 8; ++t) {
+                const float4 v = xv[t];
+                xk[4 * t + 0] = v.x;
+                xk[4 * t + 1] = v.y;
+                xk[4 * t + 2] = v.z;
+                xk[4 * t + 3] = v.w;
+            }
+#pragma unroll
+            for (int i = 0; i < NM * R; ++i) {
+                acc[i] += unit_block_dot<F, k>(U[i], xk);
+                // Materialize the sum here: otherwise the compiler sinks the
+                // work of later rows past earlier reductions and keeps every
+                // block's activations live in registers.
+                asm volatile("" : "+v"(acc[i]));
+            }
+        });
+        const int row0 = (pass * S + seg) * R;
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            float v0 = segment_sum(acc[r], u, L);
+            if constexpr (PAIR) {
+                float v1 = segment_sum(acc[R + r], u, L);
+                if (active && u == 0 && row0 + r < N) y[row0 + r] = gelu_tanh(v0) * v1;
+            } else {
+                if (active && u == 0 && row0 + r < N) y[row0 + r] = v0;
+            }
+        }
+        pass += wave_stride;
+        if (pass < npasses) load(pass);
+    }
+}
+
+// --------------------------------------------------------- generic kernel
+// Any K % 32 == 0 (K % 256 == 0 for Q4_K).  One wave per row, lanes stride
+// over the row's blocks, activations read from global memory.  Rows need
+// not be 16-byte aligned; Q4_0 / Q8_0 blocks are read with 16-bit loads.
+template <int F>
+__device__ __forceinline__ float generic_block_dot(const uint8_t* __restrict__ row, int64_t b,
+                                                   const float* __restrict__ x) {
+    if constexpr (F == kQ4_0) {
+        const uint16_t* p = reinterpret_cast<const uint16_t*>(row + 18 * b);
+        const float d = half_bits_to_float(p[0]);
+        const float* xb = x + 32 * b;
+        float s = 0.f;
+#pragma unroll
+        for (int h = 0; h < 8; ++h) {
+            const uint32_t two = p[1 + h];
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const int byte = (two >> (8 * i)) & 0xff;
+                s = fmaf(static_cast<float>((byte & 15) - 8), xb[2 * h + i], s);
+                s = fmaf(static_cast<float>((byte >> 4) - 8), xb[16 + 2 * h + i], s);
+            }
+        }
+        return d * s;
+    } else if constexpr (F == kQ8_0) {
+        const uint16_t* p = reinterpret_cast<const uint16_t*>(row + 34 * b);
+        const float d = half_bits_to_float(p[0]);
+        const float* xb = x + 32 * b;
+        float s = 0.f;
+#pragma unroll
+        for (int h = 0; h < 16; ++h) {
+            const uint32_t two = p[1 + h];
+            s = fmaf(static_cast<float>(static_cast<int8_t>(two & 0xff)), xb[2 * h], s);
+            s = fmaf(static_cast<float>(static_cast<int8_t>(two >> 8)), xb[2 * h + 1], s);
+        }
+        return d * s;
+    } else {
+        const uint4* src = reinterpret_cast<const uint4*>(row + 144 * b);
+        uint32_t U[36];
+#pragma unroll
+        for (int t = 0; t < 9; ++t) {
+            const uint4 v = src[t];
+            U[4 * t] = v.x; U[4 * t + 1] = v.y; U[4 * t + 2] = v.z; U[4 * t + 3] = v.w;
+        }
+        const float* xb = x + 256 * b;
+        float s = 0.f;
+        static_for<8>([&](auto jc) {
+            constexpr int j = decltype(jc)::value;
+            s += q4_k_sub_dot<j>(U, xb + 32 * j);
+        });
+        return s;
+    }
+}
+
+template <int F, bool PAIR>
+__global__ __launch_bounds__(kBlockThreads)
+void gemv_generic_kernel(const uint8_t* __restrict__ W0, const uint8_t* __restrict__ W1,
+                         const float* __restrict__ x, float* __restrict__ y,
+                         int N, int64_t nblocks, int64_t row_bytes) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave_stride = gridDim.x * kWavesPerBlock;
+    for (int row = blockIdx.x * kWavesPerBlock + threadIdx.x / kWave; row < N; row += wave_stride) {
+        float a0 = 0.f, a1 = 0.f;
+        for (int64_t b = lane; b < nblocks; b += kWave) {
+            a0 += generic_block_dot<F>(W0 + row * row_bytes, b, x);
+            if constexpr (PAIR) a1 += generic_block_dot<F>(W1 + row * row_bytes, b, x);
+        }
+        a0 = wave_sum(a0);
+        if constexpr (PAIR) a1 = wave_sum(a1);
+        if (lane == 0) {
+            if constexpr (PAIR) y[row] = gelu_tanh(a0) * a1;
+            else y[row] = a0;
+        }
+    }
+}
+
+template <int F, int R, bool PAIR>
+hipError_t launch_unit(const void* W0, const void* W1, const float* x, float* y, int N, int G,
+                       hipStream_t stream) {
+    const int S = kWave / G;
+    const int rows_per_pass = S * R;
+    const int npasses = (N + rows_per_pass - 1) / rows_per_pass;
+    const int max_blocks = device_cus() * 8;
+    int blocks = (npasses + kWavesPerBlock - 1) / kWavesPerBlock;
+    if (blocks > max_blocks) blocks = max_blocks;
+    const size_t lds = static_cast<size_t>(G) * kXsStride * sizeof(float);
+    hipLaunchKernelGGL((gemv_unit_kernel<F, R, PAIR>), dim3(blocks), dim3(kBlockThreads), lds, stream,
+                       static_cast<const uint8_t*>(W0), static_cast<const uint8_t*>(W1), x, y,
+                       N, G, S, npasses);
+    return hipGetLastError();
+}
+
+template <int F, bool PAIR>
+hipError_t launch_generic(const void* W0, const void* W1, const float* x, float* y, int N, int64_t K,
+                          hipStream_t stream) {
+    const int64_t per = (F == kQ4_K) ? 256 : 32;
+    const int64_t bytes = (F == kQ4_0) ? 18 : (F == kQ8_0 ? 34 : 144);
+    const int64_t nb = K / per;
+    const int max_blocks = device_cus() * 8;
+    int blocks = (N + kWavesPerBlock - 1) / kWavesPerBlock;
+    if (blocks > max_blocks) blocks = max_blocks;
+    hipLaunchKernelGGL((gemv_generic_kernel<F, PAIR>), dim3(blocks), dim3(kBlockThreads), 0, stream,
+                       static_cast<const uint8_t*>(W0), static_cast<const uint8_t*>(W1), x, y,
+                       N, nb, nb * bytes);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+int device_cus() {
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cached[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        cached[dev] = n;
+    }
+    return cached[dev];
+}
+
+// Largest K the unit kernels take: the padded activation slices must fit in
+// 64 KiB of LDS per workgroup (63 units = 65,520 B).
+constexpr int64_t kUnitMaxG = 63;
+
+hipError_t launch_gemv(int fmt, const void* W, const void* W_up, const float* x, float* y,
+                       int64_t N64, int64_t K, hipStream_t stream) {
+    const int N = static_cast<int>(N64);
+    const bool unit = (K % kUnitElems == 0) && (K / kUnitElems <= kUnitMaxG);
+    const int G = static_cast<int>(K / kUnitElems);
+    if (W_up != nullptr) {
+        return unit ? launch_unit<kQ4_0, 1, true>(W, W_up, x, y, N, G, stream)
+                    : launch_generic<kQ4_0, true>(W, W_up, x, y, N, K, stream);
+    }
+    switch (fmt) {
+    case kQ4_0:
+        return unit ? launch_unit<kQ4_0, 2, false>(W, nullptr, x, y, N, G, stream)
+                    : launch_generic<kQ4_0, false>(W, nullptr, x, y, N, K, stream);
+    case kQ8_0:
+        return unit ? launch_unit<kQ8_0, 1, false>(W, nullptr, x, y, N, G, stream)
+                    : launch_generic<kQ8_0, false>(W, nullptr, x, y, N, K, stream);
+    default:
+        return unit ? launch_unit<kQ4_K, 1, false>(W, nullptr, x, y, N, G, stream)
+                    : launch_generic<kQ4_K, false>(W, nullptr, x, y, N, K, stream);
+    }
+}
+
+}  // namespace qmv

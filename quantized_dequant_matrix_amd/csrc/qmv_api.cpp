@@ -1,0 +1,193 @@
+// C ABI of libqmv.so: argument checking and dispatch.  Every check runs on
+// the host before anything is enqueued; on any error nothing is launched.
+// The checks follow the dispatcher contract the "Metal kernel capability
+// table" (section 9) asks for: legal dimensions are checked at dispatch, a
+// path may not silently drop work, silent truncation is a defect (findings
+// F6, F13, F17 there).
+#include "../../include/qmv.h"
+
+#include <hip/hip_runtime_api.h>
+#include <stdint.h>
+
+#include "qmv_internal.h"
+
+namespace {
+
+constexpr int64_t kMaxN = (int64_t{1} << 31) - 1;
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+// a * b without int64 overflow (a, b >= 0)
+bool mul_ok(int64_t a, int64_t b, int64_t* out) {
+    if (a != 0 && b > INT64_MAX / a) return false;
+    *out = a * b;
+    return true;
+}
+
+// Shape rules common to every weight matrix: N rows of K weights, M rows of
+// activations.  elems is the weights per block (32, or 256 for Q4_K) and
+// bytes the bytes per block.
+int check_shape(int64_t N, int64_t K, int64_t M, int64_t elems, int64_t bytes) {
+    if (N < 1 || M < 1 || K < 32) return QMV_ERR_SHAPE;
+    if (K % 32 != 0 || K % elems != 0) return QMV_ERR_SHAPE;
+    if (N > kMaxN || K > kMaxN) return QMV_ERR_SHAPE;
+    int64_t t;
+    if (!mul_ok(N, (K / elems) * bytes, &t)) return QMV_ERR_SHAPE;  // weight bytes
+    if (!mul_ok(M, K, &t) || !mul_ok(t, 4, &t)) return QMV_ERR_SHAPE;  // activation bytes
+    if (!mul_ok(M, N, &t) || !mul_ok(t, 8, &t)) return QMV_ERR_SHAPE;  // output / candidate bytes
+    return QMV_OK;
+}
+
+int launched(hipError_t e) { return e == hipSuccess ? QMV_OK : QMV_ERR_LAUNCH; }
+
+int gemv(int fmt, const void* W, const void* W_up, const float* x, float* y, int64_t N, int64_t K, int64_t M,
+         hipStream_t stream) {
+    if (!W || !x || !y) return QMV_ERR_NULL;
+    const int64_t elems = (fmt == 2) ? 256 : 32;
+    const int64_t bytes = (fmt == 0) ? 18 : (fmt == 1 ? 34 : 144);
+    int rc = check_shape(N, K, M, elems, bytes);
+    if (rc) return rc;
+    if (!aligned(W, 16) || (W_up && !aligned(W_up, 16)) || !aligned(x, 4) || !aligned(y, 4)) return QMV_ERR_ALIGN;
+    for (int64_t m = 0; m < M; ++m) {
+        rc = launched(qmv::launch_gemv(fmt, W, W_up, x + m * K, y + m * N, N, K, stream));
+        if (rc) return rc;
+    }
+    return QMV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* qmv_status_str(int status) {
+    switch (status) {
+    case QMV_OK: return "ok";
+    case QMV_ERR_NULL: return "null pointer";
+    case QMV_ERR_SHAPE: return "invalid shape (N, M >= 1; K >= 32, K % 32 == 0, K % 256 == 0 for Q4_K; no overflow)";
+    case QMV_ERR_ALIGN: return "misaligned buffer (W and workspace 16 B, float/int32 buffers 4 B)";
+    case QMV_ERR_WORKSPACE: return "workspace too small";
+    case QMV_ERR_LAUNCH: return "kernel launch failed";
+    case QMV_ERR_ARG: return "argument out of range";
+    default: return "unknown status";
+    }
+}
+
+int qmv_q4_0(const void* W, const float* x, float* y, int64_t N, int64_t K, int64_t M, hipStream_t stream) {
+    return gemv(0, W, nullptr, x, y, N, K, M, stream);
+}
+
+int qmv_q8_0(const void* W, const float* x, float* y, int64_t N, int64_t K, int64_t M, hipStream_t stream) {
+    return gemv(1, W, nullptr, x, y, N, K, M, stream);
+}
+
+int qmv_q4_k(const void* W, const float* x, float* y, int64_t N, int64_t K, int64_t M, hipStream_t stream) {
+    return gemv(2, W, nullptr, x, y, N, K, M, stream);
+}
+
+int qmv_q4_0_geglu(const void* W_gate, const void* W_up, const float* x, float* h, int64_t N, int64_t K,
+                   int64_t M, hipStream_t stream) {
+    if (!W_up) return QMV_ERR_NULL;
+    return gemv(0, W_gate, W_up, x, h, N, K, M, stream);
+}
+
+size_t qmm_q4_0_q8act_ws_bytes(int64_t K, int64_t M) {
+    if (K < 32 || M < 1 || K % 32 != 0 || K > kMaxN) return 0;
+    int64_t t;
+    if (!mul_ok(M, K, &t) || !mul_ok(t, 2, &t)) return 0;
+    return qmv::qmm_ws_bytes(K, M);
+}
+
+static int qmm_split_ws(int64_t K, int64_t M, void* ws, size_t ws_bytes, int8_t** q, float** d) {
+    if (!ws) return QMV_ERR_NULL;
+    if (!aligned(ws, 16)) return QMV_ERR_ALIGN;
+    const size_t need = qmm_q4_0_q8act_ws_bytes(K, M);
+    if (need == 0) return QMV_ERR_SHAPE;
+    if (ws_bytes < need) return QMV_ERR_WORKSPACE;
+    const size_t qbytes = (static_cast<size_t>(M) * static_cast<size_t>(K) + 255) & ~static_cast<size_t>(255);
+    *q = static_cast<int8_t*>(ws);
+    *d = reinterpret_cast<float*>(static_cast<char*>(ws) + qbytes);
+    return QMV_OK;
+}
+
+int qmm_q4_0_q8act(const void* W, const float* x, float* y, int64_t N, int64_t K, int64_t M, void* ws,
+                   size_t ws_bytes, hipStream_t stream) {
+    if (!W || !x || !y) return QMV_ERR_NULL;
+    int rc = check_shape(N, K, M, 32, 18);
+    if (rc) return rc;
+    if (!aligned(W, 16) || !aligned(x, 4) || !aligned(y, 4)) return QMV_ERR_ALIGN;
+    int8_t* q;
+    float* d;
+    rc = qmm_split_ws(K, M, ws, ws_bytes, &q, &d);
+    if (rc) return rc;
+    rc = launched(qmv::launch_quantize_q8(x, q, d, K, M, stream));
+    if (rc) return rc;
+    return launched(qmv::launch_qmm(W, q, d, y, nullptr, N, K, M, stream));
+}
+
+size_t logits_topk_ws_bytes(int64_t N, int64_t M, int32_t k) {
+    if (N < 1 || M < 1 || k < 1 || N > kMaxN) return 0;
+    int64_t t;
+    if (!mul_ok(M, N, &t) || !mul_ok(t, 8 * static_cast<int64_t>(k), &t)) return 0;
+    return qmv::topk_ws_bytes(N, M, k);
+}
+
+static int check_topk_args(int64_t N, int64_t M, int32_t k, float softcap, const float* top_val,
+                           const int32_t* top_idx, void* ws, size_t ws_bytes) {
+    if (!top_val || !top_idx || !ws) return QMV_ERR_NULL;
+    if (M > 65535) return QMV_ERR_SHAPE;
+    if (k < 1 || k > 64 || k > N) return QMV_ERR_ARG;
+    if (!(softcap > 0.0f) || !(softcap <= 3.4028234663852886e38f)) return QMV_ERR_ARG;
+    if (!aligned(top_val, 4) || !aligned(top_idx, 4) || !aligned(ws, 16)) return QMV_ERR_ALIGN;
+    const size_t need = logits_topk_ws_bytes(N, M, k);
+    if (need == 0) return QMV_ERR_SHAPE;
+    if (ws_bytes < need) return QMV_ERR_WORKSPACE;
+    return QMV_OK;
+}
+
+int logits_topk(const void* W_q8_0, const float* x, float* top_val, int32_t* top_idx, int64_t N, int64_t K,
+                int64_t M, int32_t k, float softcap, void* ws, size_t ws_bytes, hipStream_t stream) {
+    if (!W_q8_0 || !x) return QMV_ERR_NULL;
+    int rc = check_shape(N, K, M, 32, 34);
+    if (rc) return rc;
+    rc = check_topk_args(N, M, k, softcap, top_val, top_idx, ws, ws_bytes);
+    if (rc) return rc;
+    if (!aligned(W_q8_0, 16) || !aligned(x, 4)) return QMV_ERR_ALIGN;
+    float* y = static_cast<float*>(ws);
+    for (int64_t m = 0; m < M; ++m) {
+        rc = launched(qmv::launch_gemv(1, W_q8_0, nullptr, x + m * K, y + m * N, N, K, stream));
+        if (rc) return rc;
+    }
+    return launched(qmv::launch_topk(y, top_val, top_idx, N, M, k, softcap, ws, stream));
+}
+
+int qmvdbg_quantize_q8(const float* x, int8_t* q, float* d, int64_t K, int64_t M, hipStream_t stream) {
+    if (!x || !q || !d) return QMV_ERR_NULL;
+    if (K < 32 || K % 32 != 0 || M < 1 || K > kMaxN) return QMV_ERR_SHAPE;
+    int64_t t;
+    if (!mul_ok(M, K, &t) || !mul_ok(t, 4, &t)) return QMV_ERR_SHAPE;
+    if (!aligned(x, 4) || !aligned(d, 4)) return QMV_ERR_ALIGN;
+    return launched(qmv::launch_quantize_q8(x, q, d, K, M, stream));
+}
+
+int qmvdbg_q4_0_q8_blocksums(const void* W, const int8_t* qx, int32_t* isum, int64_t N, int64_t K, int64_t M,
+                             hipStream_t stream) {
+    if (!W || !qx || !isum) return QMV_ERR_NULL;
+    int rc = check_shape(N, K, M, 32, 18);
+    if (rc) return rc;
+    int64_t t;
+    if (!mul_ok(M, N, &t) || !mul_ok(t, (K / 32) * 4, &t)) return QMV_ERR_SHAPE;
+    if (!aligned(W, 16) || !aligned(qx, 16) || !aligned(isum, 4)) return QMV_ERR_ALIGN;
+    return launched(qmv::launch_qmm(W, qx, nullptr, nullptr, isum, N, K, M, stream));
+}
+
+int qmvdbg_topk_f32(const float* y, float* top_val, int32_t* top_idx, int64_t N, int64_t M, int32_t k,
+                    float softcap, void* ws, size_t ws_bytes, hipStream_t stream) {
+    if (!y) return QMV_ERR_NULL;
+    if (N < 1 || M < 1 || N > kMaxN) return QMV_ERR_SHAPE;
+    int rc = check_topk_args(N, M, k, softcap, top_val, top_idx, ws, ws_bytes);
+    if (rc) return rc;
+    if (!aligned(y, 4)) return QMV_ERR_ALIGN;
+    return launched(qmv::launch_topk(y, top_val, top_idx, N, M, k, softcap, ws, stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,34 @@
+// Host-side internal interface between the C ABI (qmv_api.cpp) and the
+// kernel translation units.  Arguments reaching these functions have already
+// been validated.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace qmv {
+
+// Compute units of the current device (cached per device id).
+int device_cus();
+
+// One matrix-vector product (one activation row).  fmt: 0 Q4_0, 1 Q8_0,
+// 2 Q4_K.  W_up != nullptr selects the gated pair (Q4_0 only):
+// y = gelu(W x) * (W_up x).
+hipError_t launch_gemv(int fmt, const void* W, const void* W_up, const float* x, float* y,
+                       int64_t N, int64_t K, hipStream_t stream);
+
+// Top-k over y[M][N] (float32), candidates in ws.
+size_t topk_ws_bytes(int64_t N, int64_t M, int k);
+hipError_t launch_topk(const float* y, float* top_val, int32_t* top_idx, int64_t N, int64_t M,
+                       int k, float softcap, void* ws, hipStream_t stream);
+
+// Q4_0 x Q8 activations.
+size_t qmm_ws_bytes(int64_t K, int64_t M);
+hipError_t launch_quantize_q8(const float* x, int8_t* q, float* d, int64_t K, int64_t M,
+                              hipStream_t stream);
+// isum != nullptr: write int32 block sums [M][N][K/32] instead of y.
+hipError_t launch_qmm(const void* W, const int8_t* qx, const float* dx, float* y, int32_t* isum,
+                      int64_t N, int64_t K, int64_t M, hipStream_t stream);
+
+}  // namespace qmv

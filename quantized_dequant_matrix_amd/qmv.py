@@ -1,0 +1,127 @@
+"""Python binding of libqmv.so (argument marshalling only).
+
+Every function has the name and argument order of the C entry point declared
+in include/qmv.h.  Buffer arguments are torch tensors on the GPU (or raw
+device addresses as ints); sizes are ints; ``stream`` is a torch stream (None:
+torch's current stream).  A non-zero status raises QmvError.  All compute
+happens in the HIP kernels of libqmv.so; there is no fallback of any kind.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch  # loaded first so that libqmv.so binds to torch's HIP runtime
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libqmv.so")
+if not os.path.exists(_LIB_PATH):
+    raise ImportError(f"{_LIB_PATH} is not built; run `python -m quantized_dequant_matrix_amd.build`")
+
+lib = ctypes.CDLL(_LIB_PATH)
+
+_P = ctypes.c_void_p
+_I64 = ctypes.c_int64
+_I32 = ctypes.c_int32
+_SZ = ctypes.c_size_t
+_F = ctypes.c_float
+
+_SIGS = {
+    "qmv_status_str": ([ctypes.c_int], ctypes.c_char_p),
+    "qmv_q4_0": ([_P, _P, _P, _I64, _I64, _I64, _P], ctypes.c_int),
+    "qmv_q8_0": ([_P, _P, _P, _I64, _I64, _I64, _P], ctypes.c_int),
+    "qmv_q4_k": ([_P, _P, _P, _I64, _I64, _I64, _P], ctypes.c_int),
+    "qmv_q4_0_geglu": ([_P, _P, _P, _P, _I64, _I64, _I64, _P], ctypes.c_int),
+    "qmm_q4_0_q8act_ws_bytes": ([_I64, _I64], _SZ),
+    "qmm_q4_0_q8act": ([_P, _P, _P, _I64, _I64, _I64, _P, _SZ, _P], ctypes.c_int),
+    "logits_topk_ws_bytes": ([_I64, _I64, _I32], _SZ),
+    "logits_topk": ([_P, _P, _P, _P, _I64, _I64, _I64, _I32, _F, _P, _SZ, _P], ctypes.c_int),
+    "qmvdbg_quantize_q8": ([_P, _P, _P, _I64, _I64, _P], ctypes.c_int),
+    "qmvdbg_q4_0_q8_blocksums": ([_P, _P, _P, _I64, _I64, _I64, _P], ctypes.c_int),
+    "qmvdbg_topk_f32": ([_P, _P, _P, _I64, _I64, _I32, _F, _P, _SZ, _P], ctypes.c_int),
+}
+for _name, (_args, _res) in _SIGS.items():
+    _fn = getattr(lib, _name)
+    _fn.argtypes = _args
+    _fn.restype = _res
+
+EXPORTS = tuple(_SIGS)
+
+QMV_OK, QMV_ERR_NULL, QMV_ERR_SHAPE, QMV_ERR_ALIGN, QMV_ERR_WORKSPACE, QMV_ERR_LAUNCH, QMV_ERR_ARG = range(7)
+
+
+class QmvError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {status_str(status)} (status {status})")
+
+
+def status_str(status: int) -> str:
+    return lib.qmv_status_str(status).decode()
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(s):
+    if s is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(s, int):
+        return s
+    return s.cuda_stream
+
+
+def _call(name: str, *args) -> None:
+    rc = getattr(lib, name)(*args)
+    if rc != QMV_OK:
+        raise QmvError(rc, name)
+
+
+def qmv_q4_0(W, x, y, N, K, M=1, stream=None):
+    _call("qmv_q4_0", _ptr(W), _ptr(x), _ptr(y), N, K, M, _stream(stream))
+
+
+def qmv_q8_0(W, x, y, N, K, M=1, stream=None):
+    _call("qmv_q8_0", _ptr(W), _ptr(x), _ptr(y), N, K, M, _stream(stream))
+
+
+def qmv_q4_k(W, x, y, N, K, M=1, stream=None):
+    _call("qmv_q4_k", _ptr(W), _ptr(x), _ptr(y), N, K, M, _stream(stream))
+
+
+def qmv_q4_0_geglu(W_gate, W_up, x, h, N, K, M=1, stream=None):
+    _call("qmv_q4_0_geglu", _ptr(W_gate), _ptr(W_up), _ptr(x), _ptr(h), N, K, M, _stream(stream))
+
+
+def qmm_q4_0_q8act_ws_bytes(K, M) -> int:
+    return int(lib.qmm_q4_0_q8act_ws_bytes(K, M))
+
+
+def qmm_q4_0_q8act(W, x, y, N, K, M, ws, ws_bytes, stream=None):
+    _call("qmm_q4_0_q8act", _ptr(W), _ptr(x), _ptr(y), N, K, M, _ptr(ws), ws_bytes, _stream(stream))
+
+
+def logits_topk_ws_bytes(N, M, k) -> int:
+    return int(lib.logits_topk_ws_bytes(N, M, k))
+
+
+def logits_topk(W_q8_0, x, top_val, top_idx, N, K, M, k, softcap, ws, ws_bytes, stream=None):
+    _call("logits_topk", _ptr(W_q8_0), _ptr(x), _ptr(top_val), _ptr(top_idx), N, K, M, k, softcap,
+          _ptr(ws), ws_bytes, _stream(stream))
+
+
+def qmvdbg_quantize_q8(x, q, d, K, M, stream=None):
+    _call("qmvdbg_quantize_q8", _ptr(x), _ptr(q), _ptr(d), K, M, _stream(stream))
+
+
+def qmvdbg_q4_0_q8_blocksums(W, qx, isum, N, K, M, stream=None):
+    _call("qmvdbg_q4_0_q8_blocksums", _ptr(W), _ptr(qx), _ptr(isum), N, K, M, _stream(stream))
+
+
+def qmvdbg_topk_f32(y, top_val, top_idx, N, M, k, softcap, ws, ws_bytes, stream=None):
+    _call("qmvdbg_topk_f32", _ptr(y), _ptr(top_val), _ptr(top_idx), N, M, k, softcap, _ptr(ws), ws_bytes,
+          _stream(stream))

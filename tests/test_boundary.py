@@ -1,0 +1,117 @@
+"""The C-ABI library loads, exports every entry point include/qmv.h declares,
+and rejects bad arguments on the host before touching the GPU.
+
+No compute call is made here: EVERY call below must fail argument checking
+(the fake addresses are never valid device memory), so a new case must be
+one that the host-side checks reject."""
+import os
+import re
+
+import pytest
+
+from quantized_dequant_matrix_amd import qmv
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "qmv.h")
+
+OK, NUL, SHAPE, ALIGN, WS, LAUNCH, ARG = range(7)
+FAKE = 1 << 20          # a non-null, 256-byte aligned address that is never dereferenced here
+S = None                # null stream
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[A-Za-z_][\w\s\*]*?\b([a-z_][a-z0-9_]*)\s*\(", text, flags=re.M)))
+
+
+def test_every_declared_symbol_is_exported_and_bound():
+    names = declared_functions()
+    assert "qmv_q4_0" in names and "logits_topk" in names and len(names) == 12
+    for n in names:
+        assert hasattr(qmv.lib, n), n
+    assert sorted(qmv.EXPORTS) == names
+
+
+def test_status_strings():
+    for s in range(7):
+        assert qmv.status_str(s)
+    assert qmv.status_str(99) == "unknown status"
+
+
+def call(name, *args):
+    return getattr(qmv.lib, name)(*args)
+
+
+@pytest.mark.parametrize("name", ["qmv_q4_0", "qmv_q8_0", "qmv_q4_k"])
+def test_gemv_validation(name):
+    assert call(name, None, FAKE, FAKE, 8, 256, 1, S) == NUL
+    assert call(name, FAKE, None, FAKE, 8, 256, 1, S) == NUL
+    assert call(name, FAKE, FAKE, None, 8, 256, 1, S) == NUL
+    assert call(name, FAKE, FAKE, FAKE, 0, 256, 1, S) == SHAPE
+    assert call(name, FAKE, FAKE, FAKE, 8, 256, 0, S) == SHAPE
+    assert call(name, FAKE, FAKE, FAKE, 8, 0, 1, S) == SHAPE
+    assert call(name, FAKE, FAKE, FAKE, 8, 16, 1, S) == SHAPE
+    assert call(name, FAKE, FAKE, FAKE, 8, 33 * 32 + 1, 1, S) == SHAPE
+    assert call(name, FAKE, FAKE, FAKE, 1 << 31, 256, 1, S) == SHAPE
+    assert call(name, FAKE, FAKE, FAKE, 8, 1 << 21, 1 << 41, S) == SHAPE  # M*K*4 overflows int64
+    assert call(name, FAKE + 8, FAKE, FAKE, 8, 256, 1, S) == ALIGN
+    assert call(name, FAKE, FAKE + 2, FAKE, 8, 256, 1, S) == ALIGN
+    assert call(name, FAKE, FAKE, FAKE + 1, 8, 256, 1, S) == ALIGN
+
+
+def test_q4_k_needs_whole_superblocks():
+    assert call("qmv_q4_k", FAKE, FAKE, FAKE, 8, 288, 1, S) == SHAPE
+
+
+def test_geglu_validation():
+    assert call("qmv_q4_0_geglu", FAKE, None, FAKE, FAKE, 8, 256, 1, S) == NUL
+    assert call("qmv_q4_0_geglu", None, FAKE, FAKE, FAKE, 8, 256, 1, S) == NUL
+    assert call("qmv_q4_0_geglu", FAKE, FAKE + 4, FAKE, FAKE, 8, 256, 1, S) == ALIGN
+    assert call("qmv_q4_0_geglu", FAKE, FAKE, FAKE, FAKE, 8, 48, 1, S) == SHAPE
+
+
+def test_qmm_validation_and_workspace():
+    need = qmv.qmm_q4_0_q8act_ws_bytes(21504, 512)
+    assert need >= 512 * 21504 + 512 * 672 * 4
+    assert qmv.qmm_q4_0_q8act_ws_bytes(33, 1) == 0
+    assert qmv.qmm_q4_0_q8act_ws_bytes(64, 0) == 0
+    assert call("qmm_q4_0_q8act", FAKE, FAKE, FAKE, 8, 64, 1, None, 1 << 20, S) == NUL
+    assert call("qmm_q4_0_q8act", FAKE, FAKE, FAKE, 8, 64, 1, FAKE, 16, S) == WS
+    assert call("qmm_q4_0_q8act", FAKE, FAKE, FAKE, 8, 64, 1, FAKE + 4, 1 << 20, S) == ALIGN
+    assert call("qmm_q4_0_q8act", FAKE, FAKE, FAKE, 8, 40, 1, FAKE, 1 << 20, S) == SHAPE
+    assert call("qmm_q4_0_q8act", None, FAKE, FAKE, 8, 64, 1, FAKE, 1 << 20, S) == NUL
+
+
+def test_logits_topk_validation():
+    need = qmv.logits_topk_ws_bytes(262144, 1, 10)
+    assert need >= 262144 * 4
+    args = lambda **kw: dict(dict(W=FAKE, x=FAKE, v=FAKE, i=FAKE, N=1000, K=64, M=1, k=10, cap=30.0,
+                                  ws=FAKE, wsb=1 << 30), **kw)
+
+    def run(**kw):
+        a = args(**kw)
+        return call("logits_topk", a["W"], a["x"], a["v"], a["i"], a["N"], a["K"], a["M"], a["k"],
+                    a["cap"], a["ws"], a["wsb"], S)
+
+    assert run(W=None) == NUL
+    assert run(ws=None) == NUL
+    assert run(i=None) == NUL
+    assert run(k=0) == ARG
+    assert run(k=65) == ARG
+    assert run(N=5, k=6) == ARG
+    assert run(cap=0.0) == ARG
+    assert run(cap=-1.0) == ARG
+    assert run(cap=float("inf")) == ARG
+    assert run(cap=float("nan")) == ARG
+    assert run(wsb=16) == WS
+    assert run(ws=FAKE + 8) == ALIGN
+    assert run(i=FAKE + 2) == ALIGN
+    assert run(K=48) == SHAPE
+    assert run(M=70000) == SHAPE
+
+
+def test_debug_entry_validation():
+    assert call("qmvdbg_quantize_q8", FAKE, FAKE, FAKE, 40, 1, S) == SHAPE
+    assert call("qmvdbg_quantize_q8", None, FAKE, FAKE, 64, 1, S) == NUL
+    assert call("qmvdbg_q4_0_q8_blocksums", FAKE, FAKE + 4, FAKE, 8, 64, 1, S) == ALIGN
+    assert call("qmvdbg_topk_f32", FAKE, FAKE, FAKE, 100, 1, 101, 30.0, FAKE, 1 << 20, S) == ARG

@@ -1,0 +1,181 @@
+"""Parity of the HIP matrix-vector kernels (Q4_0, Q8_0, Q4_K, gated pair)
+with the float64 oracle, element by element, through the C ABI.
+
+Bar: |y - y_ref| <= 1e-5 * sum_i |w_i x_i| + 1e-6 for every output; the
+gated pair uses the first-order propagation of that bound (oracle.geglu_tol).
+"""
+import numpy as np
+import pytest
+
+import oracle
+from quantized_dequant_matrix_amd import synth
+from gpu_util import assert_within, dev, empty, host, say
+
+pytestmark = pytest.mark.gpu
+
+FMTS = ["q4_0", "q8_0", "q4_k"]
+
+
+def _qmv():
+    from quantized_dequant_matrix_amd import qmv
+    return qmv
+
+
+def run_gemv(fmt, W, x, N, K, M=1):
+    qmv = _qmv()
+    y = empty((M, N))
+    getattr(qmv, "qmv_" + fmt)(dev(W), dev(x), y, N, K, M)
+    return host(y)
+
+
+# (N, K): tails in N, K on and off the 256-weight units, the unit-kernel
+# limit K = 16128 and just past it, and the workload shapes.
+SHAPES = [(1, 256), (5, 512), (64, 256), (65, 256), (3, 768), (100, 1024), (33, 4096), (129, 5376),
+          (17, 16128), (9, 16384), (8, 16640), (7, 32), (11, 96), (13, 5408), (257, 2048)]
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("N,K", SHAPES)
+def test_shapes(fmt, N, K):
+    if fmt == "q4_k" and K % 256:
+        pytest.skip("Q4_K needs K % 256 == 0")
+    seed = 7 * N + K
+    say(f"qmv_{fmt} N={N} K={K} seed={seed}")
+    W, x = synth.problem(fmt, N, K, 1, seed)
+    y = run_gemv(fmt, W, x, N, K)
+    yr, S = oracle.qmv(fmt, W, N, K, x)
+    assert_within(y, yr, oracle.float_tol(S), f"qmv_{fmt} {N}x{K}")
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_batched_rows(fmt):
+    N, K, M = 77, 1280, 3
+    say(f"qmv_{fmt} M={M}")
+    W, x = synth.problem(fmt, N, K, M, 99)
+    y = run_gemv(fmt, W, x, N, K, M)
+    yr, S = oracle.qmv(fmt, W, N, K, x, M=M)
+    assert_within(y, yr, oracle.float_tol(S), f"qmv_{fmt} M={M}")
+
+
+@pytest.mark.parametrize("name,fmt", [("c1", "q4_0"), ("c2", "q4_0"), ("c5", "q4_k")])
+def test_workloads_full(name, fmt):
+    c = synth.CONFIGS[name]
+    say(f"qmv_{fmt} workload {name} N={c['N']} K={c['K']}")
+    W, x = synth.config_problem(name)
+    y = run_gemv(fmt, W, x, c["N"], c["K"])
+    yr, S = oracle.qmv(fmt, W, c["N"], c["K"], x)
+    w = assert_within(y, yr, oracle.float_tol(S), name)
+    say(f"{name}: worst err/tol {w:.3g}")
+
+
+def test_logit_workload_rows_sampled():
+    # the 262,144 x 5376 Q8_0 GEMV itself (the top-k test checks all rows)
+    c = synth.CONFIGS["c3"]
+    say("qmv_q8_0 logit workload, 4096 sampled rows")
+    W, x = synth.config_problem("c3")
+    y = run_gemv("q8_0", W, x, c["N"], c["K"])
+    rows = np.random.default_rng(0).choice(c["N"], 4096, replace=False)
+    yr, S = oracle.qmv("q8_0", W, c["N"], c["K"], x, rows=rows)
+    assert_within(y[:, rows], yr, oracle.float_tol(S), "c3 rows")
+
+
+@pytest.mark.parametrize("fmt,K", [("q4_0", 512), ("q8_0", 512), ("q4_k", 512), ("q4_0", 96), ("q8_0", 160)])
+def test_unit_vectors_give_columns(fmt, K):
+    N = 70
+    say(f"qmv_{fmt} unit vectors K={K}")
+    W, _ = synth.problem(fmt, N, K, 1, 5)
+    rb = oracle.row_bytes(fmt, K)
+    cols = [c for c in (0, 1, 15, 16, 17, 31, 32, 255) if c < K] + [K - 1]
+    E = np.zeros((len(cols), K), dtype=np.float32)
+    for j, i in enumerate(cols):
+        E[j, i] = 1.0
+    y = run_gemv(fmt, W, E, N, K, len(cols))
+    dq = np.stack([oracle.dequant_row(fmt, W[n * rb:(n + 1) * rb], K) for n in range(N)])
+    ref = dq[:, cols].T
+    if fmt == "q4_k":
+        # d*scale*q - dmin*min is exact in float64 and rounded once to float32
+        ref = ref.astype(np.float32)
+    assert np.array_equal(y, ref)
+
+
+def test_zero_weights_exactly_zero():
+    N, K = 50, 5376
+    say("qmv_q4_0 all-zero weights")
+    blk = np.frombuffer(np.array([3.0], np.float16).tobytes() + bytes([0x88] * 16), np.uint8)
+    W = np.tile(blk, N * K // 32)
+    x = np.random.default_rng(1).standard_normal((1, K)).astype(np.float32) * 1e3
+    y = run_gemv("q4_0", W, x, N, K)
+    assert np.all(y == 0.0)
+
+
+def test_wide_dynamic_range():
+    N, K = 40, 4096
+    say("qmv wide dynamic range activations")
+    for fmt in FMTS:
+        W, x = synth.problem(fmt, N, K, 1, 3)
+        x = (x * (10.0 ** np.random.default_rng(2).uniform(-15, 15, x.shape))).astype(np.float32)
+        y = run_gemv(fmt, W, x, N, K)
+        yr, S = oracle.qmv(fmt, W, N, K, x)
+        assert_within(y, yr, oracle.float_tol(S), f"{fmt} dynamic range")
+
+
+def test_deterministic_repeats():
+    c = synth.CONFIGS["c2"]
+    say("qmv_q4_0 20 repeats, bit identity")
+    qmv = _qmv()
+    W, x = synth.config_problem("c2")
+    Wd, xd = dev(W), dev(x)
+    outs = []
+    for _ in range(20):
+        y = empty((1, c["N"]))
+        qmv.qmv_q4_0(Wd, xd, y, c["N"], c["K"], 1)
+        outs.append(host(y))
+    for o in outs[1:]:
+        assert np.array_equal(o, outs[0])
+
+
+# ------------------------------------------------------------ gated pair
+def run_geglu(Wg, Wu, x, N, K, M=1):
+    qmv = _qmv()
+    h = empty((M, N))
+    qmv.qmv_q4_0_geglu(dev(Wg), dev(Wu), dev(x), h, N, K, M)
+    return host(h)
+
+
+def geglu_ref(Wg, Wu, x, N, K, M=1):
+    g, Sg = oracle.qmv("q4_0", Wg, N, K, x, M=M)
+    u, Su = oracle.qmv("q4_0", Wu, N, K, x, M=M)
+    h = oracle.geglu(g, u).reshape(g.shape)
+    return h, oracle.geglu_tol(g, u, Sg, Su, h)
+
+
+@pytest.mark.parametrize("N,K", [(1, 256), (65, 5376), (7, 96), (31, 16640), (300, 4096)])
+def test_geglu_shapes(N, K):
+    say(f"qmv_q4_0_geglu N={N} K={K}")
+    Wg, x = synth.problem("q4_0", N, K, 1, N + K)
+    Wu = synth.q4_0_weights(N, K, N + K + 1)
+    h = run_geglu(Wg, Wu, x, N, K)
+    hr, tol = geglu_ref(Wg, Wu, x, N, K)
+    assert_within(h, hr, tol, f"geglu {N}x{K}")
+
+
+def test_geglu_batched_and_large_gate():
+    N, K, M = 50, 1024, 2
+    say("qmv_q4_0_geglu M=2, large gate values")
+    Wg, x = synth.problem("q4_0", N, K, M, 11)
+    Wu = synth.q4_0_weights(N, K, 12)
+    x[1] *= 1e4          # pushes g far into both saturated ends of gelu
+    h = run_geglu(Wg, Wu, x, N, K, M)
+    hr, tol = geglu_ref(Wg, Wu, x, N, K, M)
+    assert np.all(np.isfinite(h))
+    assert_within(h, hr, tol, "geglu batched")
+
+
+def test_geglu_workload_full():
+    c = synth.CONFIGS["c2"]
+    say("qmv_q4_0_geglu workload pair 21504x5376")
+    Wg, Wu, x = synth.gate_up_problem()
+    h = run_geglu(Wg, Wu, x, c["N"], c["K"])
+    hr, tol = geglu_ref(Wg, Wu, x, c["N"], c["K"])
+    w = assert_within(h, hr, tol, "c2 pair")
+    say(f"c2 pair: worst err/tol {w:.3g}")

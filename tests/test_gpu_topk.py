@@ -1,0 +1,128 @@
+"""Parity of the logit projection + soft-cap + two-stage top-k.
+
+The logits themselves are checked element by element against the oracle
+(they are left in the workspace).  The selection is checked bit for bit
+against the oracle's full sort of the GPU's own logits, and the index set
+against the oracle's logits: identical whenever the gap between the k-th and
+(k+1)-th reference logit exceeds twice the float tolerance, otherwise every
+chosen index must be within that band of the k-th value (several sets are
+then correct)."""
+import numpy as np
+import pytest
+
+import oracle
+from quantized_dequant_matrix_amd import synth
+from gpu_util import assert_within, dev, empty, host, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _qmv():
+    from quantized_dequant_matrix_amd import qmv
+    return qmv
+
+
+def run_logits_topk(W, x, N, K, M, k, cap=30.0):
+    qmv = _qmv()
+    wsb = qmv.logits_topk_ws_bytes(N, M, k)
+    import torch
+    ws = torch.empty(wsb, dtype=torch.uint8, device="cuda:0")
+    vals = empty((M, k))
+    idx = empty((M, k), dtype=torch.int32)
+    qmv.logits_topk(dev(W), dev(x), vals, idx, N, K, M, k, cap, ws, wsb)
+    y = host(ws[: M * N * 4].view(torch.float32).reshape(M, N))
+    return host(vals), host(idx), y
+
+
+def check_selection(idx, vals, y_gpu, y_ref, S, k, cap, what):
+    # 1. the GPU ranked its own logits exactly like the oracle's full sort
+    own = oracle.topk(y_gpu.astype(np.float64), k)
+    assert idx.tolist() == own.tolist(), f"{what}: selection differs from a full sort of the GPU logits"
+    # 2. values are the capped logits
+    zr = oracle.softcap(y_ref[idx], cap)
+    T = oracle.float_tol(S)
+    assert_within(vals, zr, T[idx] + 1e-5, f"{what} values")
+    # 3. the index set against the oracle's logits
+    ref = oracle.topk(y_ref, k)
+    kth = y_ref[ref[-1]]
+    nxt = y_ref[oracle.topk(y_ref, k + 1)[-1]] if k < y_ref.size else -np.inf
+    band = 2 * T.max()
+    if kth - nxt >= band:
+        assert sorted(idx.tolist()) == sorted(ref.tolist()), f"{what}: index set differs (margin {kth - nxt:.3g})"
+    else:
+        assert np.all(y_ref[idx] >= kth - band)
+        omitted = np.ones(y_ref.size, dtype=bool)
+        omitted[idx] = False
+        assert np.all(y_ref[omitted] <= kth + band)
+    return kth - nxt
+
+
+def test_logit_workload():
+    c = synth.CONFIGS["c3"]
+    N, K, k, cap = c["N"], c["K"], c["k"], c["softcap"]
+    say(f"logits_topk workload N={N} K={K} k={k}")
+    W, x = synth.config_problem("c3")
+    vals, idx, y = run_logits_topk(W, x, N, K, 1, k, cap)
+    yr, S = oracle.qmv("q8_0", W, N, K, x)
+    w = assert_within(y, yr, oracle.float_tol(S), "c3 logits")
+    margin = check_selection(idx[0], vals[0], y[0], yr[0], S[0], k, cap, "c3")
+    say(f"c3: worst logit err/tol {w:.3g}, k-th margin {margin:.4g}")
+
+
+@pytest.mark.parametrize("N,K,M,k", [(1, 64, 1, 1), (100, 256, 1, 7), (4096, 512, 1, 10), (4097, 512, 2, 64),
+                                     (9000, 96, 1, 33), (20000, 1024, 3, 1)])
+def test_shapes(N, K, M, k):
+    say(f"logits_topk N={N} K={K} M={M} k={k}")
+    W, x = synth.problem("q8_0", N, K, M, N + k)
+    vals, idx, y = run_logits_topk(W, x, N, K, M, k)
+    yr, S = oracle.qmv("q8_0", W, N, K, x, M=M)
+    assert_within(y, yr, oracle.float_tol(S), "logits")
+    for m in range(M):
+        check_selection(idx[m], vals[m], y[m], yr[m], S[m], k, 30.0, f"m={m}")
+
+
+def test_duplicate_rows_tie_to_lower_index():
+    N, K, k = 6000, 512, 12
+    say("logits_topk duplicated rows")
+    W, x = synth.problem("q8_0", N, K, 1, 5)
+    rb = oracle.row_bytes("q8_0", K)
+    yr, _ = oracle.qmv("q8_0", W, N, K, x)
+    best = int(np.argmax(yr[0]))
+    Wm = W.reshape(N, rb).copy()
+    dup = [4500, 17, 5999, 4096, 4095, 300]
+    Wm[dup] = Wm[best]
+    vals, idx, y = run_logits_topk(Wm.reshape(-1), x, N, K, 1, k)
+    group = sorted(dup + [best])
+    assert np.all(y[0, group] == y[0, best]), "identical rows must give identical logits"
+    assert idx[0, :len(group)].tolist() == group
+
+
+def test_nan_inf_and_signed_zero_order():
+    qmv = _qmv()
+    import torch
+    say("qmvdbg_topk_f32 special values")
+    rng = np.random.default_rng(3)
+    N, k = 10000, 64
+    y = rng.standard_normal(N).astype(np.float32)
+    y[rng.choice(N, 40, replace=False)] = np.nan
+    y[[5, 9000]] = np.inf
+    y[[6, 7]] = -np.inf
+    y[100:130] = 0.0
+    y[130:160] = -0.0
+    y[200:230] = 3.0
+    wsb = qmv.logits_topk_ws_bytes(N, 1, k)
+    ws = torch.empty(wsb, dtype=torch.uint8, device="cuda:0")
+    vals = empty((1, k))
+    idx = empty((1, k), dtype=torch.int32)
+    qmv.qmvdbg_topk_f32(dev(y), vals, idx, N, 1, k, 30.0, ws, wsb)
+    got = host(idx)[0]
+    assert got.tolist() == oracle.topk(y.astype(np.float64), k).tolist()
+    # all-NaN tail: ask for every element of a short vector
+    z = np.array([np.nan, 1.0, np.nan, -0.0, 0.0, -np.inf], np.float32)
+    vals = empty((1, 6))
+    idx = empty((1, 6), dtype=torch.int32)
+    qmv.qmvdbg_topk_f32(dev(z), vals, idx, 6, 1, 6, 30.0, ws, wsb)
+    assert host(idx)[0].tolist() == oracle.topk(z.astype(np.float64), 6).tolist() == [1, 3, 4, 5, 0, 2]
+    v = host(vals)[0]
+    assert v[0] == np.float32(30.0 * np.tanh(1.0 / 30.0)) or abs(v[0] - 30 * np.tanh(1 / 30)) < 1e-6
+    assert v[3] == -30.0 and np.isnan(v[4]) and np.isnan(v[5])
