@@ -21,6 +21,7 @@ from __future__ import annotations
 import argparse
 import json
 import os
+import re
 import sys
 import time
 
@@ -29,6 +30,38 @@ import numpy as np
 HBM_PEAK_GBS = 8000.0  # MI355X published HBM3E bandwidth
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
+
+# HBM traffic per launch comes from the committed rocprofv3 counter summary
+# (FETCH_SIZE / WRITE_SIZE, scaled by a plain copy); it is reported only while
+# the sources it was measured on are unchanged.
+TRAFFIC_PROFILE = os.path.join("profiles", "qmv_bench_workloads_hbm_traffic.md")
+# kernel symbol and workgroup count of each timed launch at N=21504, K=5376
+KERNEL_OF = {
+    "qmv_q4_0": ("qmv::gemv_unit_kernel<0, 2, false>", 896),
+    "qmv_q4_0_geglu": ("qmv::gemv_unit_kernel<0, 1, true>", 1792),
+}
+
+
+def profiled_traffic(kernel: str, grid: int):
+    """HBM bytes (read + write) per launch of `kernel` from the counter
+    summary, or None when it is missing or was taken on other sources."""
+    import hashlib
+    path = os.path.join(ROOT, TRAFFIC_PROFILE)
+    try:
+        text = open(path).read()
+    except OSError:
+        return None
+    for src, digest in re.findall(r"source_sha256 (\S+) ([0-9a-f]{64})", text):
+        try:
+            with open(os.path.join(ROOT, src), "rb") as f:
+                if hashlib.sha256(f.read()).hexdigest() != digest:
+                    return None
+        except OSError:
+            return None
+    for name, g, rd, wr in re.findall(r"<!-- traffic (.+?) grid=(\d+) read=(\d+) write=(\d+) -->", text):
+        if name == kernel and int(g) == grid:
+            return int(rd) + int(wr)
+    return None
 
 
 def parse():
@@ -40,11 +73,29 @@ def parse():
     p.add_argument("--no-rows", action="store_true", help="skip the per-row measurements of the other workloads")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
+    p.add_argument("--copy-calibration", type=int, default=0, metavar="MB",
+                   help="only run 10 device-to-device copies of MB megabytes (a plain copy kernel of known "
+                        "size, used to scale the HBM traffic counters) and exit")
     return p.parse_args()
+
+
+def copy_calibration(mb: int) -> None:
+    import torch
+    n = mb * 1000 * 1000
+    a = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    for _ in range(10):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_per_copy": n, "copies": 10}))
 
 
 def main():
     args = parse()
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the path has no multi-GPU part "
               "in this build", file=sys.stderr)
@@ -107,23 +158,21 @@ def main():
     t_pair = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
 
     value = bytes_step / (ms_step * 1e-3) / 1e9
-    kernels = {
-        "qmv_q4_0 (gemv_unit_kernel<Q4_0,2,false>)": {
-            "bytes": bytes_single, "us": t_single * 1e3,
-            "GB/s": bytes_single / (t_single * 1e-3) / 1e9},
-        "qmv_q4_0_geglu (gemv_unit_kernel<Q4_0,1,true>)": {
-            "bytes": bytes_pair, "us": t_pair * 1e3,
-            "GB/s": bytes_pair / (t_pair * 1e-3) / 1e9},
-    }
-    dom_name, dom = max(kernels.items(), key=lambda kv: kv[1]["us"])
+    kernels = {}
+    for entry, b, tk in (("qmv_q4_0", bytes_single, t_single), ("qmv_q4_0_geglu", bytes_pair, t_pair)):
+        sym, grid = KERNEL_OF[entry]
+        kernels[entry] = {"kernel": sym, "workgroups": grid, "bytes": b, "us": round(tk * 1e3, 3),
+                          "GB/s": round(b / (tk * 1e-3) / 1e9, 1), "hbm_traffic_bytes": profiled_traffic(sym, grid)}
+    dom_entry, dom = max(kernels.items(), key=lambda kv: kv[1]["us"])
     roofline = {
         "bound": "hbm",
-        "kernel": dom_name,
-        "achieved": round(dom["GB/s"], 1),
+        "kernel": f"{dom_entry} ({dom['kernel']})",
+        "achieved": dom["GB/s"],
         "peak": HBM_PEAK_GBS,
         "unit": "GB/s",
         "frac": round(dom["GB/s"] / HBM_PEAK_GBS, 4),
-        "traffic": None,
+        "traffic": dom["hbm_traffic_bytes"],
+        "traffic_source": TRAFFIC_PROFILE if dom["hbm_traffic_bytes"] is not None else None,
     }
 
     rows = None

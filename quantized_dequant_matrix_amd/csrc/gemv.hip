@@ -46,13 +46,14 @@ __device__ __forceinline__ void static_for(Fn&& fn) {
 
 // ---------------------------------------------------------------- Q4_0
 // Block k (0..7) of a 144-byte unit U[36]: fp16 d at byte 18k, codes at
-// bytes 18k+2 .. 18k+17.  Returns d/16 * sum_j 16 (q_j - 8) x_j.
+// bytes 18k+2 .. 18k+17.  Returns d * sum_j 16 (q_j - 8) x_j (16x the block's
+// contribution; the caller scales the row sum by 1/16, exactly).
 template <int k>
 __device__ __forceinline__ float q4_0_block_dot(const uint32_t* U, const float* xk) {
     constexpr int b0 = 18 * k;
     constexpr int dwd = b0 >> 2;
     const uint32_t dbits = ((b0 & 3) == 2) ? (U[dwd] >> 16) : (U[dwd] & 0xffffu);
-    const float d16 = half_bits_to_float(dbits) * 0.0625f;
+    const float d = half_bits_to_float(dbits);  // the factor 1/16 is applied once per row
     constexpr int qb = b0 + 2;
     uint32_t qs[4];
 #pragma unroll
@@ -63,22 +64,23 @@ __device__ __forceinline__ float q4_0_block_dot(const uint32_t* U, const float* 
             qs[t] = shift16(U[(qb >> 2) + t + 1], U[(qb >> 2) + t]);
         }
     }
-    float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
+    float s0 = 0.f, s1 = 0.f;
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-        const uint32_t v = qs[t] ^ 0x88888888u;
-        const uint32_t hi = v & 0xF0F0F0F0u;          // elements 16+4t+i
-        const uint32_t lo = (v << 4) & 0xF0F0F0F0u;   // elements 4t+i
+        // 16 (q - 8) as signed bytes: flip the code's top bit, keep the
+        // nibble in the high half of each byte (one bitop3 each on gfx950)
+        const uint32_t hi = (qs[t] ^ 0x88888888u) & 0xF0F0F0F0u;          // elements 16+4t+i
+        const uint32_t lo = ((qs[t] << 4) ^ 0x88888880u) & 0xF0F0F0F0u;   // elements 4t+i
         s0 = fmaf(sbyte<0>(lo), xk[4 * t + 0], s0);
         s1 = fmaf(sbyte<1>(lo), xk[4 * t + 1], s1);
-        s2 = fmaf(sbyte<2>(lo), xk[4 * t + 2], s2);
-        s3 = fmaf(sbyte<3>(lo), xk[4 * t + 3], s3);
+        s0 = fmaf(sbyte<2>(lo), xk[4 * t + 2], s0);
+        s1 = fmaf(sbyte<3>(lo), xk[4 * t + 3], s1);
         s0 = fmaf(sbyte<0>(hi), xk[16 + 4 * t + 0], s0);
         s1 = fmaf(sbyte<1>(hi), xk[16 + 4 * t + 1], s1);
-        s2 = fmaf(sbyte<2>(hi), xk[16 + 4 * t + 2], s2);
-        s3 = fmaf(sbyte<3>(hi), xk[16 + 4 * t + 3], s3);
+        s0 = fmaf(sbyte<2>(hi), xk[16 + 4 * t + 2], s0);
+        s1 = fmaf(sbyte<3>(hi), xk[16 + 4 * t + 3], s1);
     }
-    return d16 * ((s0 + s1) + (s2 + s3));
+    return d * (s0 + s1);
 }
 
 // ---------------------------------------------------------------- Q8_0
@@ -90,13 +92,13 @@ __device__ __forceinline__ float q8_0_block_dot(const uint32_t* U, const float* 
     constexpr int dwd = b0 >> 2;
     const uint32_t dbits = ((b0 & 3) == 2) ? (U[dwd] >> 16) : (U[dwd] & 0xffffu);
     const float d = half_bits_to_float(dbits);
-    float s[4] = {0.f, 0.f, 0.f, 0.f};
+    float s[2] = {0.f, 0.f};
     static_for<32>([&](auto ec) {
         constexpr int e = decltype(ec)::value;
         constexpr int pos = b0 + 2 + e;
-        s[e & 3] = fmaf(sbyte<pos & 3>(U[pos >> 2]), xk[e], s[e & 3]);
+        s[e & 1] = fmaf(sbyte<pos & 3>(U[pos >> 2]), xk[e], s[e & 1]);
     });
-    return d * ((s[0] + s[1]) + (s[2] + s[3]));
+    return d * (s[0] + s[1]);
 }
 
 // ---------------------------------------------------------------- Q4_K
@@ -117,17 +119,17 @@ __device__ __forceinline__ float q4_k_sub_dot(const uint32_t* U, const float* xk
     const float a = half_bits_to_float(U[0] & 0xffffu) * static_cast<float>(sc);  // exact
     const float nb = -(half_bits_to_float(U[0] >> 16) * static_cast<float>(mn));  // exact
     constexpr int c = j >> 1;
-    float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
+    float s0 = 0.f, s1 = 0.f;
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
         const uint32_t raw = U[4 + 8 * c + t];
         const uint32_t q = (j & 1) ? ((raw >> 4) & 0x0F0F0F0Fu) : (raw & 0x0F0F0F0Fu);
         s0 = fmaf(fmaf(a, ubyte<0>(q), nb), xk[4 * t + 0], s0);
         s1 = fmaf(fmaf(a, ubyte<1>(q), nb), xk[4 * t + 1], s1);
-        s2 = fmaf(fmaf(a, ubyte<2>(q), nb), xk[4 * t + 2], s2);
-        s3 = fmaf(fmaf(a, ubyte<3>(q), nb), xk[4 * t + 3], s3);
+        s0 = fmaf(fmaf(a, ubyte<2>(q), nb), xk[4 * t + 2], s0);
+        s1 = fmaf(fmaf(a, ubyte<3>(q), nb), xk[4 * t + 3], s1);
     }
-    return (s0 + s1) + (s2 + s3);
+    return s0 + s1;
 }
 
 template <int F, int k>
@@ -137,11 +139,40 @@ __device__ __forceinline__ float unit_block_dot(const uint32_t* U, const float* 
     else return q4_k_sub_dot<k>(U, xk);
 }
 
-// Stage x[0..K) into LDS as G padded unit slices.
+// Stage x[0..K) into LDS as G padded unit slices.  Each thread issues a batch
+// of loads before the matching LDS writes (indices past the end are clamped
+// to the last element, which is then written twice with the same value), so a
+// workgroup waits for a couple of memory round trips, not one per element.
+constexpr int kMaxUnits = 63;
 __device__ __forceinline__ void stage_x(float* xs, const float* __restrict__ x, int G) {
-    const int n = G * kUnitElems;
-    for (int i = threadIdx.x; i < n; i += kBlockThreads) {
-        xs[(i >> 8) * kXsStride + (i & 255)] = x[i];
+    if ((reinterpret_cast<uintptr_t>(x) & 15) == 0) {
+        constexpr int kPer = 4;  // 16-byte loads in flight per thread
+        const int n4 = G * (kUnitElems / 4);
+        for (int base = 0; base < n4; base += kPer * kBlockThreads) {
+            float4 v[kPer];
+#pragma unroll
+            for (int j = 0; j < kPer; ++j) {
+                const int i = min(base + j * kBlockThreads + static_cast<int>(threadIdx.x), n4 - 1);
+                v[j] = reinterpret_cast<const float4*>(x)[i];
+            }
+#pragma unroll
+            for (int j = 0; j < kPer; ++j) {
+                const int i = min(base + j * kBlockThreads + static_cast<int>(threadIdx.x), n4 - 1);
+                *reinterpret_cast<float4*>(xs + (i >> 6) * kXsStride + (i & 63) * 4) = v[j];
+            }
+        }
+    } else {
+        const int n = G * kUnitElems;
+        for (int base = 0; base < n; base += 16 * kBlockThreads) {
+            float v[16];
+#pragma unroll
+            for (int j = 0; j < 16; ++j) v[j] = x[min(base + j * kBlockThreads + static_cast<int>(threadIdx.x), n - 1)];
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+                const int i = min(base + j * kBlockThreads + static_cast<int>(threadIdx.x), n - 1);
+                xs[(i >> 8) * kXsStride + (i & 255)] = v[j];
+            }
+        }
     }
 }
 
@@ -172,24 +203,21 @@ void gemv_unit_kernel(const uint8_t* __restrict__ W0, const uint8_t* __restrict_
     auto load = [&](int p) {
 #pragma unroll
         for (int r = 0; r < R; ++r) {
-            const int row = (p * S + seg) * R + r;
-            const bool ok = active && row < N;
+            // Rows past the end (and lanes outside every segment) load the
+            // last row again: valid memory, results never stored.
+            int row = (p * S + seg) * R + r;
+            row = row < N ? row : N - 1;
 #pragma unroll
             for (int m = 0; m < NM; ++m) {
-                if (ok) {
-                    const uint8_t* base = (m == 0 ? W0 : W1) + row * row_bytes + u * UB;
-                    const uint4* src = reinterpret_cast<const uint4*>(base);
+                const uint8_t* base = (m == 0 ? W0 : W1) + row * row_bytes + u * UB;
+                const uint4* src = reinterpret_cast<const uint4*>(base);
 #pragma unroll
-                    for (int t = 0; t < VEC; ++t) {
-                        const uint4 v = src[t];
-                        U[m * R + r][4 * t + 0] = v.x;
-                        U[m * R + r][4 * t + 1] = v.y;
-                        U[m * R + r][4 * t + 2] = v.z;
-                        U[m * R + r][4 * t + 3] = v.w;
-                    }
-                } else {
-#pragma unroll
-                    for (int t = 0; t < 4 * VEC; ++t) U[m * R + r][t] = 0u;
+                for (int t = 0; t < VEC; ++t) {
+                    const uint4 v = src[t];
+                    U[m * R + r][4 * t + 0] = v.x;
+                    U[m * R + r][4 * t + 1] = v.y;
+                    U[m * R + r][4 * t + 2] = v.z;
+                    U[m * R + r][4 * t + 3] = v.w;
                 }
             }
         }
@@ -232,11 +260,12 @@ void gemv_unit_kernel(const uint8_t* __restrict__ W0, const uint8_t* __restrict_
             }
         });
         const int row0 = (pass * S + seg) * R;
+        constexpr float kScale = (F == kQ4_0) ? 0.0625f : 1.0f;
 #pragma unroll
         for (int r = 0; r < R; ++r) {
-            float v0 = segment_sum(acc[r], u, L);
+            float v0 = segment_sum(acc[r], u, L) * kScale;
             if constexpr (PAIR) {
-                float v1 = segment_sum(acc[R + r], u, L);
+                float v1 = segment_sum(acc[R + r], u, L) * kScale;
                 if (active && u == 0 && row0 + r < N) y[row0 + r] = gelu_tanh(v0) * v1;
             } else {
                 if (active && u == 0 && row0 + r < N) y[row0 + r] = v0;
@@ -369,7 +398,7 @@ int device_cus() {
 
 // Largest K the unit kernels take: the padded activation slices must fit in
 // 64 KiB of LDS per workgroup (63 units = 65,520 B).
-constexpr int64_t kUnitMaxG = 63;
+constexpr int64_t kUnitMaxG = kMaxUnits;
 
 hipError_t launch_gemv(int fmt, const void* W, const void* W_up, const float* x, float* y,
                        int64_t N64, int64_t K, hipStream_t stream) {
