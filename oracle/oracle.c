@@ -358,7 +358,7 @@ int oracle_qmm_q4_0_q8(const uint8_t* W, int64_t N, int64_t K,
 /* Reading (order): value descending, equal values -> lower index       */
 /* first, NaN after every number (NaNs among themselves by index).      */
 /* Merge sort of indices: stable and independent of qsort's order.      */
-/* Pinned against a brute-force selection in tests/test_oracle_topk.py. */
+/* Pinned against a brute-force selection in tests/test_oracle_special.py. */
 /* ------------------------------------------------------------------ */
 static int before(const double* v, int32_t a, int32_t b) {
     /* strict "a ranks before b" */
