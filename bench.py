@@ -258,7 +258,7 @@ def measure_rows(torch, qmv, synth, dev):
     for M in c["Ms"]:
         x = synth.activations(M, K, synth.SEEDS["c4"])
         xd, y = t(x), torch.empty((M, N), device=dev)
-        wsb = qmv.qmm_q4_0_q8act_ws_bytes(K, M)
+        wsb = qmv.qmm_q4_0_q8act_ws_bytes(N, K, M)
         ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
         iters = 100 if M < 512 else 5
         ms = _time_loop(torch, lambda i: qmv.qmm_q4_0_q8act(slots[i % 8], xd, y, N, K, M, ws, wsb), iters,

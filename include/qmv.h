@@ -107,13 +107,17 @@ int qmv_q4_0_geglu(const void* W_gate, const void* W_up, const float* x, float* 
  *   amax == 0 -> d_x = 0 and q = 0;
  * the int8 codes and scales go to the workspace.  Step 2 forms the exact
  * int32 block sums isum = sum_j (q_w - 8) * q_x with integer dot products
- * (int8 MFMA for M >= 16) and accumulates y += isum * d_w * d_x in float32.
+ * (v_dot4 for M == 1, int8 MFMA for M >= 2) and accumulates
+ * y += isum * d_w * d_x in float32.
  * Activations must be finite.
  * [captable section 1: q4_matvec_v4, Q4_0 x Q8 int8 + scales; section 2:
  *  quantize_q8; roadmap K3: batched Q4_0 matrix-matrix kernels for prefill]
- * ws: device buffer of at least qmm_q4_0_q8act_ws_bytes(K, M) bytes,
- * 16-byte aligned, contents overwritten. */
-size_t qmm_q4_0_q8act_ws_bytes(int64_t K, int64_t M);
+ * ws: device buffer of at least qmm_q4_0_q8act_ws_bytes(N, K, M) bytes,
+ * 16-byte aligned, contents overwritten.  It holds the int8 codes and
+ * scales of x (rows padded to the kernel's tile height) and, when the
+ * contraction splits K across workgroups (small M), the float32 partial
+ * sums.  The size depends on (N, K, M) only; 0 means an invalid shape. */
+size_t qmm_q4_0_q8act_ws_bytes(int64_t N, int64_t K, int64_t M);
 int qmm_q4_0_q8act(const void* W, const float* x, float* y,
                    int64_t N, int64_t K, int64_t M,
                    void* ws, size_t ws_bytes, hipStream_t stream);

@@ -5,11 +5,16 @@
 // Step 1 (quantize_q8_kernel): every 32-element block of x gets
 //   d = max|x| / 127 (IEEE float32 division), q = clamp(round(x / d), +-127)
 // (round half away from zero; an all-zero block gives d = 0, q = 0).
-// Step 2 (qmm_dot_kernel): exact int32 block sums
+// Step 2: exact int32 block sums
 //   isum = sum_j (q_w - 8) * q_x
-// with v_dot4_i32_i8, then y += isum * d_w * d_x in float32.  The weight
-// codes enter the dot products as 16 (q_w - 8) in a signed byte, so the dot
-// gives 16 isum exactly (|16 isum| <= 32*128*127) and the shift back is exact.
+// then y += isum * d_w * d_x in float32.  The weight codes enter the integer
+// products as 16 (q_w - 8) in a signed byte, so the sums are 16 isum exactly
+// (|16 isum| <= 32*128*127) and the shift back is exact.
+//   M == 1: qmm_dot_kernel, v_dot4_i32_i8 per lane (an HBM-bound GEMV).
+//   M >= 2: qmm_mfma_kernel, where the work is a dense int8 contraction: one
+//           v_mfma_i32_16x16x32_i8 covers exactly one block (K = 32) of a
+//           16 x 16 tile of (m, n), so every block sum stays exact and gets
+//           its own scale in the float epilogue.
 #include <utility>
 
 #include "qmv_device.h"
@@ -20,27 +25,87 @@ namespace {
 
 constexpr int kQxStride = kUnitElems + 16;  // bytes of one unit's codes in LDS (+16 B pad)
 
+// Layout of the quantized activations for the MFMA kernel ("fragment
+// layout"), with Mt = ceil(M / 16) tiles of 16 rows and nb = K / 32 blocks:
+//   codes  [Mt][nb / 2][64 lanes][16 B]: lane l = i + 16 g holds, for row
+//          16 t + i, bytes 0..7 = block 2c and bytes 8..15 = block 2c + 1,
+//          each as x[4g .. 4g+3] followed by x[16+4g .. 16+4g+3] -- the same
+//          elements as code bytes 4g .. 4g+3 of a Q4_0 block (low nibbles,
+//          then high nibbles), so one code dword of the weights pairs with
+//          one 8-byte operand of the activations;
+//   scales [Mt][nb][16] float: d_x of row 16 t + i for block b.
+// Rows M .. 16 Mt - 1 are quantized as zeros.
+struct FragLayout {
+    int64_t nb;
+    __device__ __forceinline__ int64_t code_dword(int64_t m, int64_t b, int t) const {
+        const int64_t mt = m >> 4, i = m & 15;
+        const int g = t & 3, half = t >> 2;  // t: which 4 elements of the block (4t .. 4t+3)
+        return (((mt * (nb >> 1) + (b >> 1)) * kWave + i + 16 * g) * 16 + (b & 1) * 8 + half * 4) >> 2;
+    }
+    __device__ __forceinline__ int64_t scale_index(int64_t m, int64_t b) const {
+        return ((m >> 4) * nb + b) * 16 + (m & 15);
+    }
+};
+
+// One 8-lane group per 32-element block, 4 elements per lane.  FRAG: write
+// the fragment layout (rows padded to a multiple of 16), else row-major
+// codes [M][K] and scales [M][K/32].
+template <bool FRAG>
 __global__ __launch_bounds__(kBlockThreads)
 void quantize_q8_kernel(const float* __restrict__ x, int8_t* __restrict__ q, float* __restrict__ d,
-                        int64_t total) {
-    const int64_t stride = static_cast<int64_t>(gridDim.x) * kBlockThreads;
-    for (int64_t e = static_cast<int64_t>(blockIdx.x) * kBlockThreads + threadIdx.x; e - threadIdx.x < total;
-         e += stride) {
-        const bool ok = e < total;  // total % 32 == 0: whole 32-lane groups agree
-        const float v = ok ? x[e] : 0.0f;
-        float a = fabsf(v);
+                        int64_t K, int64_t M, int64_t Mrows, bool vec_x, bool vec_q) {
+    const int64_t nb = K / 32;
+    const int64_t total = Mrows * nb;  // blocks, padding rows included
+    const int t = threadIdx.x & 7;
+    const int64_t stride = static_cast<int64_t>(gridDim.x) * (kBlockThreads / 8);
+    // the loop bound is taken per wave so that shuffles see whole groups
+    for (int64_t wave_first = (static_cast<int64_t>(blockIdx.x) * kBlockThreads + (threadIdx.x & ~(kWave - 1))) / 8;
+         wave_first < total; wave_first += stride) {
+        const int64_t blk = wave_first + (threadIdx.x & (kWave - 1)) / 8;
+        const bool ok = blk < total;
+        const int64_t m = ok ? blk / nb : 0;
+        const int64_t b = ok ? blk - m * nb : 0;
+        float v[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+        if (ok && m < M) {
+            const float* src = x + m * K + 32 * b + 4 * t;
+            if (vec_x) {
+                const float4 f = *reinterpret_cast<const float4*>(src);
+                v[0] = f.x; v[1] = f.y; v[2] = f.z; v[3] = f.w;
+            } else {
 #pragma unroll
-        for (int o = 16; o > 0; o >>= 1) a = fmaxf(a, __shfl_xor(a, o, 32));
+                for (int e = 0; e < 4; ++e) v[e] = src[e];
+            }
+        }
+        float a = fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3])));
+#pragma unroll
+        for (int o = 4; o > 0; o >>= 1) a = fmaxf(a, __shfl_xor(a, o, 8));
         const float db = a / 127.0f;
-        int qv = 0;
-        if (a != 0.0f) {
-            float t = roundf(v / db);
-            t = fminf(fmaxf(t, -127.0f), 127.0f);
-            qv = static_cast<int>(t);
+        uint32_t packed = 0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            int qv = 0;
+            if (a != 0.0f) {
+                float r = roundf(v[e] / db);
+                r = fminf(fmaxf(r, -127.0f), 127.0f);
+                qv = static_cast<int>(r);
+            }
+            packed |= (static_cast<uint32_t>(qv) & 0xffu) << (8 * e);
         }
         if (ok) {
-            q[e] = static_cast<int8_t>(qv);
-            if ((threadIdx.x & 31) == 0) d[e >> 5] = db;
+            if constexpr (FRAG) {
+                const FragLayout L{nb};
+                reinterpret_cast<uint32_t*>(q)[L.code_dword(m, b, t)] = packed;
+                if (t == 0) d[L.scale_index(m, b)] = db;
+            } else {
+                int8_t* dst = q + m * K + 32 * b + 4 * t;
+                if (vec_q) {
+                    *reinterpret_cast<uint32_t*>(dst) = packed;
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) dst[e] = static_cast<int8_t>(packed >> (8 * e));
+                }
+                if (t == 0) d[m * nb + b] = db;
+            }
         }
     }
 }
@@ -178,8 +243,9 @@ void qmm_generic_kernel(const uint8_t* __restrict__ W, const int8_t* __restrict_
     }
 }
 
-// Units per lane C and lanes per segment L = G / C: the split of a row that
-// keeps the most lanes of a wave busy (ties: fewer units per lane).
+// Units per lane C and lanes per segment L = G / C: the smallest C (so the
+// most waves) that keeps at least 54 of a wave's 64 lanes busy, else the
+// split with the most busy lanes.
 void plan_segments(int G, int* C, int* L, int* S) {
     int bestC = G, bestL = 1, best_active = 0;
     for (int c = 1; c <= G; ++c) {
@@ -187,6 +253,7 @@ void plan_segments(int G, int* C, int* L, int* S) {
         const int l = G / c;
         if (l > kWave) continue;
         const int active = (kWave / l) * l;
+        if (active >= 54) { bestC = c; bestL = l; break; }
         if (active > best_active) { best_active = active; bestC = c; bestL = l; }
     }
     *C = bestC;
@@ -194,31 +261,336 @@ void plan_segments(int G, int* C, int* L, int* S) {
     *S = kWave / bestL;
 }
 
-size_t align256(size_t b) { return (b + 255) & ~static_cast<size_t>(255); }
+// ------------------------------------------------------------ MFMA kernel
+// Tiles of (m, n) per workgroup: TM = 16 MW WM activation rows by TN = 16 NW
+// WN weight rows; four waves in a WM x WN x WK grid, each wave owning MW x NW
+// 16 x 16 sub-tiles (WK > 1: the waves split the blocks of a tile and their
+// partial sums are added in LDS, in wave order).  A workgroup covers blocks
+// [ks kb, (ks + 1) kb) of K; with several K splits it writes partial sums
+// that qmm_reduce_kernel adds in split order.
+//
+// Weights: the workgroup copies TN rows x KC blocks (raw GGUF bytes) into
+// LDS per chunk, 16-byte coalesced, prefetching the next chunk into
+// registers while it computes on this one.  Operand of lane (j = l % 16,
+// g = l / 16) for weight row j: code dword g of the block, split into the
+// low and the high nibbles as 16 (q - 8) signed bytes.  Activations come
+// from the fragment layout written by quantize_q8_kernel<true>.
+//
+// v_mfma_i32_16x16x32_i8: A 16 x 32 (lane l: row l % 16, 8 bytes of k-group
+// l / 16), B 32 x 16 (lane l: column l % 16, same k-group), D 16 x 16 int32
+// (lane l: column l % 16, rows 4 (l / 16) .. +3).  The eight k values of a
+// k-group are the same eight block elements in A and in B, so the product
+// is the block's integer sum whatever order the hardware adds them in.
+typedef int v4i __attribute__((ext_vector_type(4)));
 
-}  // namespace
+enum QmmMode : int { kModeY = 0, kModePartial = 1, kModeISum = 2 };
 
-size_t qmm_ws_bytes(int64_t K, int64_t M) {
-    return align256(static_cast<size_t>(M) * static_cast<size_t>(K)) +
-           align256(static_cast<size_t>(M) * static_cast<size_t>(K / 32) * sizeof(float));
+__device__ __forceinline__ uint64_t q4_codes_to_s8(uint32_t c) {
+    const uint32_t lo = ((c << 4) ^ 0x88888880u) & 0xF0F0F0F0u;  // elements 4g .. 4g+3
+    const uint32_t hi = (c ^ 0x88888888u) & 0xF0F0F0F0u;         // elements 16+4g .. 16+4g+3
+    return static_cast<uint64_t>(lo) | (static_cast<uint64_t>(hi) << 32);
 }
 
-hipError_t launch_quantize_q8(const float* x, int8_t* q, float* d, int64_t K, int64_t M, hipStream_t stream) {
-    const int64_t total = K * M;
-    int64_t blocks = (total + kBlockThreads - 1) / kBlockThreads;
+template <int MW, int NW, int WM, int WN, int WK, int KC, int MODE>
+__global__ __launch_bounds__(kBlockThreads)
+void qmm_mfma_kernel(const uint8_t* __restrict__ W, const int8_t* __restrict__ xa,
+                     const float* __restrict__ xd, float* __restrict__ out, int32_t* __restrict__ isum,
+                     int N, int64_t M, int nb, int64_t tm0, int64_t tiles_m, int tiles_n, int kb_per,
+                     int64_t nwg) {
+    constexpr int TN = 16 * NW * WN;
+    constexpr int RB = KC * 18;       // bytes of one weight row per chunk
+    constexpr int RS = RB + 16;       // LDS row stride: rows 4 banks apart (mod 64)
+    constexpr int PR = RB / 16;       // 16-byte pieces per row
+    constexpr int LPT = TN * PR / kBlockThreads;
+    static_assert(KC % 8 == 0 && TN * PR == LPT * kBlockThreads, "the weight chunk must split evenly");
+    static_assert(WM * WN * WK == kWavesPerBlock, "four waves per workgroup");
+    __shared__ __align__(16) uint32_t wt[TN * RS / 4];
+
+    // Consecutive workgroup ids are dealt round-robin to the 8 XCDs; give
+    // each XCD a contiguous run of tiles (same weight rows, all m-tiles) so
+    // that its L2 serves the weight reuse.
+    int64_t lin = blockIdx.x;
+    if (nwg % 8 == 0) lin = (lin % 8) * (nwg / 8) + lin / 8;
+    const int64_t tm = tm0 + lin % tiles_m;
+    lin /= tiles_m;
+    const int tn = static_cast<int>(lin % tiles_n);
+    const int ks = static_cast<int>(lin / tiles_n);
+    const int kb0 = ks * kb_per;
+    const int kb1 = min(nb, kb0 + kb_per);
+    const int n0 = tn * TN;
+    const int64_t K = static_cast<int64_t>(nb) * 32;
+    const int64_t row_bytes = static_cast<int64_t>(nb) * 18;
+
+    const int w = threadIdx.x / kWave;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wk = w % WK;
+    const int wn = (w / WK) % WN;
+    const int wm = w / (WK * WN);
+    const int li = lane & 15;
+    const int lg = lane >> 4;
+
+    uint32_t pre[LPT * 4];
+    auto fetch = [&](int c0) {
+        const int valid = min(KC, kb1 - c0) * 18;  // a multiple of 144
+#pragma unroll
+        for (int t = 0; t < LPT; ++t) {
+            const int p = t * kBlockThreads + static_cast<int>(threadIdx.x);
+            const int r = p / PR;
+            const int q = p - r * PR;
+            const int row = min(n0 + r, N - 1);             // rows past N: any valid row
+            const int off = (q * 16 < valid) ? q * 16 : 0;  // blocks past the split: any valid piece
+            const uint4 v = *reinterpret_cast<const uint4*>(W + row * row_bytes + static_cast<int64_t>(c0) * 18 + off);
+            pre[4 * t + 0] = v.x;
+            pre[4 * t + 1] = v.y;
+            pre[4 * t + 2] = v.z;
+            pre[4 * t + 3] = v.w;
+        }
+    };
+    auto stash = [&]() {
+#pragma unroll
+        for (int t = 0; t < LPT; ++t) {
+            const int p = t * kBlockThreads + static_cast<int>(threadIdx.x);
+            const int r = p / PR;
+            const int q = p - r * PR;
+            *reinterpret_cast<uint4*>(wt + r * (RS / 4) + q * 4) =
+                make_uint4(pre[4 * t], pre[4 * t + 1], pre[4 * t + 2], pre[4 * t + 3]);
+        }
+    };
+
+    float acc[MW][NW][4];
+#pragma unroll
+    for (int mi = 0; mi < MW; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < NW; ++ni)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) acc[mi][ni][r] = 0.0f;
+
+    fetch(kb0);
+    for (int c0 = kb0; c0 < kb1; c0 += KC) {
+        __syncthreads();  // every wave is done with the previous chunk
+        stash();
+        __syncthreads();
+        if (c0 + KC < kb1) fetch(c0 + KC);
+        const int npair = min(KC, kb1 - c0) >> 1;
+        for (int cp = wk; cp < npair; cp += WK) {
+            const int64_t b = c0 + 2 * cp;  // blocks b (even) and b + 1
+            uint64_t ae[MW], ao[MW];
+            float xe[MW][4], xo[MW][4];
+#pragma unroll
+            for (int mi = 0; mi < MW; ++mi) {
+                const int64_t mt = tm * (MW * WM) + wm * MW + mi;  // 16-row tile
+                if constexpr (MODE == kModeISum) {
+                    // row-major codes [M][K] (rows past M: any valid row)
+                    int64_t m = mt * 16 + li;
+                    m = m < M ? m : M - 1;
+                    const uint32_t* src = reinterpret_cast<const uint32_t*>(xa + m * K + 32 * b);
+                    ae[mi] = static_cast<uint64_t>(src[lg]) | (static_cast<uint64_t>(src[4 + lg]) << 32);
+                    ao[mi] = static_cast<uint64_t>(src[8 + lg]) | (static_cast<uint64_t>(src[12 + lg]) << 32);
+                } else {
+                    const uint4 v = *reinterpret_cast<const uint4*>(xa + ((mt * (nb >> 1) + (b >> 1)) * kWave + lane) * 16);
+                    ae[mi] = static_cast<uint64_t>(v.x) | (static_cast<uint64_t>(v.y) << 32);
+                    ao[mi] = static_cast<uint64_t>(v.z) | (static_cast<uint64_t>(v.w) << 32);
+                    const float4 de = *reinterpret_cast<const float4*>(xd + (mt * nb + b) * 16 + 4 * lg);
+                    const float4 dq = *reinterpret_cast<const float4*>(xd + (mt * nb + b + 1) * 16 + 4 * lg);
+                    xe[mi][0] = de.x; xe[mi][1] = de.y; xe[mi][2] = de.z; xe[mi][3] = de.w;
+                    xo[mi][0] = dq.x; xo[mi][1] = dq.y; xo[mi][2] = dq.z; xo[mi][3] = dq.w;
+                }
+            }
+            uint64_t be[NW], bo[NW];
+            float se[NW], so[NW];
+#pragma unroll
+            for (int ni = 0; ni < NW; ++ni) {
+                const uint32_t* rowp = wt + ((wn * NW + ni) * 16 + li) * (RS / 4) + 9 * cp;
+                // block b: codes at bytes 2 + 4g .. 5 + 4g of the pair (2 mod 4)
+                const uint32_t ce = __builtin_amdgcn_alignbyte(rowp[lg + 1], rowp[lg], 2);
+                // block b + 1: codes at bytes 20 + 4g .. (aligned)
+                const uint32_t co = rowp[5 + lg];
+                be[ni] = q4_codes_to_s8(ce);
+                bo[ni] = q4_codes_to_s8(co);
+                if constexpr (MODE != kModeISum) {
+                    se[ni] = half_bits_to_float(rowp[0] & 0xffffu) * 0.0625f;  // d of block b / 16
+                    so[ni] = half_bits_to_float(rowp[4] >> 16) * 0.0625f;      // d of block b + 1 / 16
+                }
+            }
+#pragma unroll
+            for (int mi = 0; mi < MW; ++mi) {
+#pragma unroll
+                for (int ni = 0; ni < NW; ++ni) {
+                    const v4i zero = {0, 0, 0, 0};
+                    const v4i De = __builtin_amdgcn_mfma_i32_16x16x32_i8(static_cast<long>(ae[mi]),
+                                                                          static_cast<long>(be[ni]), zero, 0, 0, 0);
+                    const v4i Do = __builtin_amdgcn_mfma_i32_16x16x32_i8(static_cast<long>(ao[mi]),
+                                                                          static_cast<long>(bo[ni]), zero, 0, 0, 0);
+                    if constexpr (MODE == kModeISum) {
+                        const int n = n0 + (wn * NW + ni) * 16 + li;
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) {
+                            const int64_t m = (tm * (MW * WM) + wm * MW + mi) * 16 + 4 * lg + r;
+                            if (m < M && n < N) {
+                                int32_t* dst = isum + (m * N + n) * nb + b;
+                                dst[0] = De[r] >> 4;
+                                dst[1] = Do[r] >> 4;
+                            }
+                        }
+                    } else {
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) {
+                            acc[mi][ni][r] = fmaf(static_cast<float>(De[r]), se[ni] * xe[mi][r], acc[mi][ni][r]);
+                            acc[mi][ni][r] = fmaf(static_cast<float>(Do[r]), so[ni] * xo[mi][r], acc[mi][ni][r]);
+                        }
+                    }
+                }
+            }
+        }
+    }
+    if constexpr (MODE != kModeISum) {
+        if constexpr (WK > 1) {
+            constexpr int NV = MW * NW * 4;
+            static_assert((WK - 1) * WM * WN * NV * kWave <= TN * RS / 4, "reduction fits the weight tile");
+            __syncthreads();  // the weight tile is free
+            float* red = reinterpret_cast<float*>(wt);
+            const int slot = wm * WN + wn;
+            if (wk > 0) {
+#pragma unroll
+                for (int v = 0; v < NV; ++v)
+                    red[(((wk - 1) * WM * WN + slot) * NV + v) * kWave + lane] = acc[v / (NW * 4)][(v / 4) % NW][v % 4];
+            }
+            __syncthreads();
+            if (wk == 0) {
+                for (int j = 1; j < WK; ++j) {
+#pragma unroll
+                    for (int v = 0; v < NV; ++v)
+                        acc[v / (NW * 4)][(v / 4) % NW][v % 4] += red[(((j - 1) * WM * WN + slot) * NV + v) * kWave + lane];
+                }
+            }
+        }
+        if (wk == 0) {
+            float* o = out + static_cast<int64_t>(ks) * M * N;
+#pragma unroll
+            for (int mi = 0; mi < MW; ++mi)
+#pragma unroll
+                for (int ni = 0; ni < NW; ++ni) {
+                    const int n = n0 + (wn * NW + ni) * 16 + li;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int64_t m = (tm * (MW * WM) + wm * MW + mi) * 16 + 4 * lg + r;
+                        if (m < M && n < N) o[m * N + n] = acc[mi][ni][r];
+                    }
+                }
+        }
+    }
+}
+
+// y = sum over K splits of the partial sums, in split order.
+__global__ __launch_bounds__(kBlockThreads)
+void qmm_reduce_kernel(const float* __restrict__ P, float* __restrict__ y, int ks, int64_t MN) {
+    const int64_t stride = static_cast<int64_t>(gridDim.x) * kBlockThreads;
+    for (int64_t i = static_cast<int64_t>(blockIdx.x) * kBlockThreads + threadIdx.x; i < MN; i += stride) {
+        float s = P[i];
+        for (int k = 1; k < ks; ++k) s += P[k * MN + i];
+        y[i] = s;
+    }
+}
+
+size_t align256(size_t b) { return (b + 255) & ~static_cast<size_t>(255); }
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Largest K whose activation codes and scales fit one workgroup's LDS in
+// qmm_dot_kernel.
+constexpr int64_t kDotMaxG = 200;
+
+// The two MFMA tilings: wide (64 x 64 per workgroup, 32 x 32 per wave) and
+// narrow (16 x 16 per workgroup, the four waves splitting K).
+#define QMM_WIDE 2, 2, 2, 2, 1, 32
+#define QMM_NARROW 1, 1, 1, 1, 4, 128
+constexpr int kWideTM = 64, kWideTN = 64, kNarrowTM = 16, kNarrowTN = 16;
+
+enum QmmPath : int { kPathDot = 0, kPathGeneric = 1, kPathWide = 2, kPathNarrow = 3 };
+
+// Everything about a call that depends only on (N, K, M): kernels, tiles,
+// K splits and the workspace parts, so that the workspace size and the
+// launches always agree.
+struct QmmPlan {
+    int path = kPathGeneric;
+    int64_t tiles_m = 0;
+    int tiles_n = 0, ks = 1, kb = 0;
+    int64_t xrows = 0;  // activation rows in the workspace (padded to the tile height)
+    size_t q_bytes = 0, d_bytes = 0, p_bytes = 0;
+};
+
+QmmPlan plan_qmm(int64_t N, int64_t K, int64_t M) {
+    QmmPlan p;
+    const int64_t nb = K / 32;
+    const bool units = K % kUnitElems == 0;
+    if (M == 1 || !units) {
+        p.path = (units && K / kUnitElems <= kDotMaxG) ? kPathDot : kPathGeneric;
+        p.xrows = M;
+    } else if (ceil_div(M, kWideTM) * ceil_div(N, kWideTN) >= 512) {
+        p.path = kPathWide;
+        p.tiles_m = ceil_div(M, kWideTM);
+        p.tiles_n = static_cast<int>(ceil_div(N, kWideTN));
+        p.ks = 1;
+        p.kb = static_cast<int>(nb);
+        p.xrows = p.tiles_m * kWideTM;
+    } else {
+        p.path = kPathNarrow;
+        p.tiles_m = ceil_div(M, kNarrowTM);
+        p.tiles_n = static_cast<int>(ceil_div(N, kNarrowTN));
+        const int64_t tiles = p.tiles_m * p.tiles_n;
+        // enough workgroups to stream the weights from every CU
+        int64_t ks = ceil_div(1024, tiles);
+        ks = ks < nb / 8 ? ks : nb / 8;
+        ks = ks > 1 ? ks : 1;
+        const int64_t kb = ceil_div(ceil_div(nb, ks), 8) * 8;
+        p.kb = static_cast<int>(kb);
+        p.ks = static_cast<int>(ceil_div(nb, kb));
+        p.xrows = p.tiles_m * kNarrowTM;
+    }
+    p.q_bytes = align256(static_cast<size_t>(p.xrows) * static_cast<size_t>(K));
+    p.d_bytes = align256(static_cast<size_t>(p.xrows) * static_cast<size_t>(nb) * sizeof(float));
+    p.p_bytes = p.ks > 1 ? align256(static_cast<size_t>(p.ks) * static_cast<size_t>(M) * static_cast<size_t>(N) *
+                                    sizeof(float))
+                         : 0;
+    return p;
+}
+
+template <bool FRAG>
+hipError_t launch_quantize(const float* x, int8_t* q, float* d, int64_t K, int64_t M, int64_t Mrows,
+                           hipStream_t stream) {
+    const int64_t groups = Mrows * (K / 32);
+    int64_t blocks = ceil_div(groups * 8, kBlockThreads);
     const int64_t cap = static_cast<int64_t>(device_cus()) * 64;
     if (blocks > cap) blocks = cap;
-    hipLaunchKernelGGL(quantize_q8_kernel, dim3(static_cast<unsigned>(blocks)), dim3(kBlockThreads), 0, stream,
-                       x, q, d, total);
+    const bool vec_x = (reinterpret_cast<uintptr_t>(x) & 15) == 0;
+    const bool vec_q = (reinterpret_cast<uintptr_t>(q) & 3) == 0;
+    hipLaunchKernelGGL((quantize_q8_kernel<FRAG>), dim3(static_cast<unsigned>(blocks)), dim3(kBlockThreads), 0,
+                       stream, x, q, d, K, M, Mrows, vec_x, vec_q);
     return hipGetLastError();
 }
 
-// Largest K whose activation codes and scales fit one workgroup's LDS.
-constexpr int64_t kDotMaxG = 200;
+template <int MW, int NW, int WM, int WN, int WK, int KC, int MODE>
+hipError_t launch_mfma(const QmmPlan& p, const void* W, const int8_t* xa, const float* xd, float* out,
+                       int32_t* isum, int64_t N, int64_t K, int64_t M, hipStream_t stream) {
+    // slices of m-tiles keep the grid within 2^30 workgroups
+    const int64_t per_mt = static_cast<int64_t>(p.tiles_n) * p.ks;
+    int64_t mt_slice = (int64_t{1} << 30) / per_mt;
+    mt_slice = mt_slice < p.tiles_m ? mt_slice : p.tiles_m;
+    for (int64_t tm0 = 0; tm0 < p.tiles_m; tm0 += mt_slice) {
+        const int64_t tms = (p.tiles_m - tm0 < mt_slice) ? p.tiles_m - tm0 : mt_slice;
+        const int64_t nwg = tms * per_mt;
+        hipLaunchKernelGGL((qmm_mfma_kernel<MW, NW, WM, WN, WK, KC, MODE>), dim3(static_cast<unsigned>(nwg)),
+                           dim3(kBlockThreads), 0, stream, static_cast<const uint8_t*>(W), xa, xd, out, isum,
+                           static_cast<int>(N), M, static_cast<int>(K / 32), tm0, tms, p.tiles_n, p.kb, nwg);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
 
-hipError_t launch_qmm(const void* W, const int8_t* qx, const float* dx, float* y, int32_t* isum,
+// The M == 1 and K % 256 != 0 paths (row-major activation codes).
+hipError_t launch_dot(const QmmPlan& p, const void* W, const int8_t* qx, const float* dx, float* y, int32_t* isum,
                       int64_t N64, int64_t K, int64_t M, hipStream_t stream) {
-    if (K % kUnitElems != 0 || K / kUnitElems > kDotMaxG) {
+    if (p.path == kPathGeneric) {
         int64_t blocks = (N64 * M + kWavesPerBlock - 1) / kWavesPerBlock;
         const int64_t cap = static_cast<int64_t>(device_cus()) * 8;
         if (blocks > cap) blocks = cap;
@@ -255,6 +627,50 @@ hipError_t launch_qmm(const void* W, const int8_t* qx, const float* dx, float* y
         if (e != hipSuccess) return e;
     }
     return hipSuccess;
+}
+
+}  // namespace
+
+size_t qmm_ws_bytes(int64_t N, int64_t K, int64_t M) {
+    const QmmPlan p = plan_qmm(N, K, M);
+    return p.q_bytes + p.d_bytes + p.p_bytes;
+}
+
+hipError_t launch_quantize_q8(const float* x, int8_t* q, float* d, int64_t K, int64_t M, hipStream_t stream) {
+    return launch_quantize<false>(x, q, d, K, M, M, stream);
+}
+
+hipError_t launch_qmm_q8act(const void* W, const float* x, float* y, int64_t N, int64_t K, int64_t M, void* ws,
+                            hipStream_t stream) {
+    const QmmPlan p = plan_qmm(N, K, M);
+    int8_t* q = static_cast<int8_t*>(ws);
+    float* d = reinterpret_cast<float*>(static_cast<char*>(ws) + p.q_bytes);
+    float* part = reinterpret_cast<float*>(static_cast<char*>(ws) + p.q_bytes + p.d_bytes);
+    const bool mfma = p.path == kPathWide || p.path == kPathNarrow;
+    hipError_t e = mfma ? launch_quantize<true>(x, q, d, K, M, p.xrows, stream)
+                        : launch_quantize<false>(x, q, d, K, M, M, stream);
+    if (e != hipSuccess) return e;
+    if (!mfma) return launch_dot(p, W, q, d, y, nullptr, N, K, M, stream);
+    if (p.path == kPathWide) return launch_mfma<QMM_WIDE, kModeY>(p, W, q, d, y, nullptr, N, K, M, stream);
+    if (p.ks == 1) return launch_mfma<QMM_NARROW, kModeY>(p, W, q, d, y, nullptr, N, K, M, stream);
+    e = launch_mfma<QMM_NARROW, kModePartial>(p, W, q, d, part, nullptr, N, K, M, stream);
+    if (e != hipSuccess) return e;
+    const int64_t MN = M * N;
+    int64_t blocks = ceil_div(MN, kBlockThreads);
+    const int64_t cap = static_cast<int64_t>(device_cus()) * 8;
+    if (blocks > cap) blocks = cap;
+    hipLaunchKernelGGL(qmm_reduce_kernel, dim3(static_cast<unsigned>(blocks)), dim3(kBlockThreads), 0, stream,
+                       part, y, p.ks, MN);
+    return hipGetLastError();
+}
+
+hipError_t launch_q4_0_q8_blocksums(const void* W, const int8_t* qx, int32_t* isum, int64_t N, int64_t K, int64_t M,
+                                    hipStream_t stream) {
+    const QmmPlan p = plan_qmm(N, K, M);
+    if (p.path == kPathWide) return launch_mfma<QMM_WIDE, kModeISum>(p, W, qx, nullptr, nullptr, isum, N, K, M, stream);
+    if (p.path == kPathNarrow)
+        return launch_mfma<QMM_NARROW, kModeISum>(p, W, qx, nullptr, nullptr, isum, N, K, M, stream);
+    return launch_dot(p, W, qx, nullptr, nullptr, isum, N, K, M, stream);
 }
 
 }  // namespace qmv

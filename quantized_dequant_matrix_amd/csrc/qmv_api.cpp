@@ -90,38 +90,19 @@ int qmv_q4_0_geglu(const void* W_gate, const void* W_up, const float* x, float* 
     return gemv(0, W_gate, W_up, x, h, N, K, M, stream);
 }
 
-size_t qmm_q4_0_q8act_ws_bytes(int64_t K, int64_t M) {
-    if (K < 32 || M < 1 || K % 32 != 0 || K > kMaxN) return 0;
-    int64_t t;
-    if (!mul_ok(M, K, &t) || !mul_ok(t, 2, &t)) return 0;
-    return qmv::qmm_ws_bytes(K, M);
-}
-
-static int qmm_split_ws(int64_t K, int64_t M, void* ws, size_t ws_bytes, int8_t** q, float** d) {
-    if (!ws) return QMV_ERR_NULL;
-    if (!aligned(ws, 16)) return QMV_ERR_ALIGN;
-    const size_t need = qmm_q4_0_q8act_ws_bytes(K, M);
-    if (need == 0) return QMV_ERR_SHAPE;
-    if (ws_bytes < need) return QMV_ERR_WORKSPACE;
-    const size_t qbytes = (static_cast<size_t>(M) * static_cast<size_t>(K) + 255) & ~static_cast<size_t>(255);
-    *q = static_cast<int8_t*>(ws);
-    *d = reinterpret_cast<float*>(static_cast<char*>(ws) + qbytes);
-    return QMV_OK;
+size_t qmm_q4_0_q8act_ws_bytes(int64_t N, int64_t K, int64_t M) {
+    if (check_shape(N, K, M, 32, 18) != QMV_OK) return 0;
+    return qmv::qmm_ws_bytes(N, K, M);
 }
 
 int qmm_q4_0_q8act(const void* W, const float* x, float* y, int64_t N, int64_t K, int64_t M, void* ws,
                    size_t ws_bytes, hipStream_t stream) {
-    if (!W || !x || !y) return QMV_ERR_NULL;
+    if (!W || !x || !y || !ws) return QMV_ERR_NULL;
     int rc = check_shape(N, K, M, 32, 18);
     if (rc) return rc;
-    if (!aligned(W, 16) || !aligned(x, 4) || !aligned(y, 4)) return QMV_ERR_ALIGN;
-    int8_t* q;
-    float* d;
-    rc = qmm_split_ws(K, M, ws, ws_bytes, &q, &d);
-    if (rc) return rc;
-    rc = launched(qmv::launch_quantize_q8(x, q, d, K, M, stream));
-    if (rc) return rc;
-    return launched(qmv::launch_qmm(W, q, d, y, nullptr, N, K, M, stream));
+    if (!aligned(W, 16) || !aligned(x, 4) || !aligned(y, 4) || !aligned(ws, 16)) return QMV_ERR_ALIGN;
+    if (ws_bytes < qmm_q4_0_q8act_ws_bytes(N, K, M)) return QMV_ERR_WORKSPACE;
+    return launched(qmv::launch_qmm_q8act(W, x, y, N, K, M, ws, stream));
 }
 
 size_t logits_topk_ws_bytes(int64_t N, int64_t M, int32_t k) {
@@ -177,7 +158,7 @@ int qmvdbg_q4_0_q8_blocksums(const void* W, const int8_t* qx, int32_t* isum, int
     int64_t t;
     if (!mul_ok(M, N, &t) || !mul_ok(t, (K / 32) * 4, &t)) return QMV_ERR_SHAPE;
     if (!aligned(W, 16) || !aligned(qx, 16) || !aligned(isum, 4)) return QMV_ERR_ALIGN;
-    return launched(qmv::launch_qmm(W, qx, nullptr, nullptr, isum, N, K, M, stream));
+    return launched(qmv::launch_q4_0_q8_blocksums(W, qx, isum, N, K, M, stream));
 }
 
 int qmvdbg_topk_f32(const float* y, float* top_val, int32_t* top_idx, int64_t N, int64_t M, int32_t k,

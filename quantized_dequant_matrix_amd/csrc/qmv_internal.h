@@ -23,12 +23,18 @@ size_t topk_ws_bytes(int64_t N, int64_t M, int k);
 hipError_t launch_topk(const float* y, float* top_val, int32_t* top_idx, int64_t N, int64_t M,
                        int k, float softcap, void* ws, hipStream_t stream);
 
-// Q4_0 x Q8 activations.
-size_t qmm_ws_bytes(int64_t K, int64_t M);
+// Q4_0 x Q8 activations.  The workspace layout (and its size) depends on
+// (N, K, M) only.
+size_t qmm_ws_bytes(int64_t N, int64_t K, int64_t M);
+// Row-major codes [M][K] and scales [M][K/32] (step 1 alone).
 hipError_t launch_quantize_q8(const float* x, int8_t* q, float* d, int64_t K, int64_t M,
                               hipStream_t stream);
-// isum != nullptr: write int32 block sums [M][N][K/32] instead of y.
-hipError_t launch_qmm(const void* W, const int8_t* qx, const float* dx, float* y, int32_t* isum,
-                      int64_t N, int64_t K, int64_t M, hipStream_t stream);
+// Both steps: quantize x into ws, then y = the scaled block sums.
+hipError_t launch_qmm_q8act(const void* W, const float* x, float* y, int64_t N, int64_t K, int64_t M,
+                            void* ws, hipStream_t stream);
+// int32 block sums [M][N][K/32] of row-major int8 activations, from the
+// kernel the same (N, K, M) selects in launch_qmm_q8act.
+hipError_t launch_q4_0_q8_blocksums(const void* W, const int8_t* qx, int32_t* isum, int64_t N,
+                                    int64_t K, int64_t M, hipStream_t stream);
 
 }  // namespace qmv

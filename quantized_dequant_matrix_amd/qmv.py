@@ -31,7 +31,7 @@ _SIGS = {
     "qmv_q8_0": ([_P, _P, _P, _I64, _I64, _I64, _P], ctypes.c_int),
     "qmv_q4_k": ([_P, _P, _P, _I64, _I64, _I64, _P], ctypes.c_int),
     "qmv_q4_0_geglu": ([_P, _P, _P, _P, _I64, _I64, _I64, _P], ctypes.c_int),
-    "qmm_q4_0_q8act_ws_bytes": ([_I64, _I64], _SZ),
+    "qmm_q4_0_q8act_ws_bytes": ([_I64, _I64, _I64], _SZ),
     "qmm_q4_0_q8act": ([_P, _P, _P, _I64, _I64, _I64, _P, _SZ, _P], ctypes.c_int),
     "logits_topk_ws_bytes": ([_I64, _I64, _I32], _SZ),
     "logits_topk": ([_P, _P, _P, _P, _I64, _I64, _I64, _I32, _F, _P, _SZ, _P], ctypes.c_int),
@@ -97,8 +97,8 @@ def qmv_q4_0_geglu(W_gate, W_up, x, h, N, K, M=1, stream=None):
     _call("qmv_q4_0_geglu", _ptr(W_gate), _ptr(W_up), _ptr(x), _ptr(h), N, K, M, _stream(stream))
 
 
-def qmm_q4_0_q8act_ws_bytes(K, M) -> int:
-    return int(lib.qmm_q4_0_q8act_ws_bytes(K, M))
+def qmm_q4_0_q8act_ws_bytes(N, K, M) -> int:
+    return int(lib.qmm_q4_0_q8act_ws_bytes(N, K, M))
 
 
 def qmm_q4_0_q8act(W, x, y, N, K, M, ws, ws_bytes, stream=None):

@@ -71,10 +71,13 @@ def test_geglu_validation():
 
 
 def test_qmm_validation_and_workspace():
-    need = qmv.qmm_q4_0_q8act_ws_bytes(21504, 512)
+    need = qmv.qmm_q4_0_q8act_ws_bytes(5376, 21504, 512)
     assert need >= 512 * 21504 + 512 * 672 * 4
-    assert qmv.qmm_q4_0_q8act_ws_bytes(33, 1) == 0
-    assert qmv.qmm_q4_0_q8act_ws_bytes(64, 0) == 0
+    # small M splits K across workgroups: partial sums [splits][M][N] join the workspace
+    assert qmv.qmm_q4_0_q8act_ws_bytes(5376, 21504, 16) > 16 * 21504 + 16 * 672 * 4 + 5376 * 16 * 4
+    assert qmv.qmm_q4_0_q8act_ws_bytes(8, 33, 1) == 0
+    assert qmv.qmm_q4_0_q8act_ws_bytes(8, 64, 0) == 0
+    assert qmv.qmm_q4_0_q8act_ws_bytes(0, 64, 1) == 0
     assert call("qmm_q4_0_q8act", FAKE, FAKE, FAKE, 8, 64, 1, None, 1 << 20, S) == NUL
     assert call("qmm_q4_0_q8act", FAKE, FAKE, FAKE, 8, 64, 1, FAKE, 16, S) == WS
     assert call("qmm_q4_0_q8act", FAKE, FAKE, FAKE, 8, 64, 1, FAKE + 4, 1 << 20, S) == ALIGN

@@ -35,7 +35,7 @@ def gpu_blocksums(W, qx, N, K, M):
 
 def gpu_qmm(W, x, N, K, M):
     qmv = _qmv()
-    wsb = qmv.qmm_q4_0_q8act_ws_bytes(K, M)
+    wsb = qmv.qmm_q4_0_q8act_ws_bytes(N, K, M)
     ws = torch.empty(wsb, dtype=torch.uint8, device="cuda:0")
     y = empty((M, N))
     qmv.qmm_q4_0_q8act(dev(W), dev(x), y, N, K, M, ws, wsb)
