@@ -30,6 +30,9 @@ FLAGS = [
     "-fhip-fp32-correctly-rounded-divide-sqrt",
     # No packed-FP32 instructions anywhere in this library.
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA results in ordinary VGPRs: the epilogue reads them with VALU ops
+    # anyway, and the AGPR form would add one copy per result
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-Wall",
     "-I", os.path.join(ROOT, "include"),
 ]

@@ -537,8 +537,11 @@ QmmPlan plan_qmm(int64_t N, int64_t K, int64_t M) {
         p.tiles_m = ceil_div(M, kNarrowTM);
         p.tiles_n = static_cast<int>(ceil_div(N, kNarrowTN));
         const int64_t tiles = p.tiles_m * p.tiles_n;
-        // enough workgroups to stream the weights from every CU
-        int64_t ks = ceil_div(1024, tiles);
+        // about 1024 workgroups: enough to stream the weights from every CU,
+        // few enough to be resident at once (4 per CU); a workgroup that
+        // signalled the others through memory would need a cache writeback
+        // per workgroup, so the splits are added by a second kernel
+        int64_t ks = 1024 / tiles;
         ks = ks < nb / 8 ? ks : nb / 8;
         ks = ks > 1 ? ks : 1;
         const int64_t kb = ceil_div(ceil_div(nb, ks), 8) * 8;

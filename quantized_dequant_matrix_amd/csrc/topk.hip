@@ -12,12 +12,18 @@
 // unique, so round r of a selection is "the largest key below the key chosen
 // in round r-1": no per-element bookkeeping is needed.
 //
-// Stage 1: every wave owns a 1024-entry chunk (16 keys per lane, in
-//          registers) and emits its k best; each round is a lane-local scan
-//          plus a DPP wave reduction, with no workgroup barrier.
-// Stage 2: one 1024-thread workgroup per activation row: each wave selects
-//          the k best of its share of the candidates, then one wave selects
-//          the k best of those and writes indices and soft-capped values.
+// Stage 1: every wave owns a chunk of 64 KPL entries (KPL keys per lane, in
+//          registers) and emits its k best, largest first; a round is a
+//          lane-local masked maximum (a tree over KPL keys) plus a DPP wave
+//          reduction, with no workgroup barrier.  KPL grows with N so that
+//          there are at most 1024 chunks.
+// Stage 2: one 1024-thread workgroup per activation row runs a tournament
+//          over the sorted chunk lists: thread t holds the head of list t
+//          (and the next few entries in registers); each round finds the
+//          workgroup maximum, and the thread that owned it moves to its next
+//          entry.  Keys are unique, so exactly one thread wins a round.
+// Very long rows (more than 4M entries, so more than 1024 chunks of 4096)
+// fall back to a merge that rescans candidates from memory every round.
 #include <stdint.h>
 
 #include "qmv_device.h"
@@ -26,11 +32,10 @@
 namespace qmv {
 namespace {
 
-constexpr int kChunk = 1024;                  // entries per wave in stage 1
-constexpr int kPerLane = kChunk / kWave;      // 16
 constexpr int kMergeThreads = 1024;
 constexpr int kMergeWaves = kMergeThreads / kWave;
-constexpr int kMergeRegs = 8;                 // candidates a lane keeps in registers in stage 2
+constexpr int kMaxLists = kMergeThreads;  // chunk lists the tournament takes
+constexpr int kListRegs = 8;              // entries of its list a merge thread keeps in registers
 
 __device__ __forceinline__ uint64_t order_key(float v, uint32_t idx) {
     uint32_t code;
@@ -48,47 +53,61 @@ __device__ __forceinline__ uint64_t umax64(uint64_t a, uint64_t b) { return a > 
 
 // Lanes the DPP pattern does not write keep 0, the identity of the max.
 template <int CTRL, int ROW_MASK>
-__device__ __forceinline__ uint64_t dpp64(uint64_t v) {
-    const uint32_t lo = static_cast<uint32_t>(
-        __builtin_amdgcn_update_dpp(0, static_cast<int>(static_cast<uint32_t>(v)), CTRL, ROW_MASK, 0xF, false));
-    const uint32_t hi = static_cast<uint32_t>(
-        __builtin_amdgcn_update_dpp(0, static_cast<int>(static_cast<uint32_t>(v >> 32)), CTRL, ROW_MASK, 0xF, false));
+__device__ __forceinline__ uint32_t dpp32(uint32_t v) {
+    return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), CTRL, ROW_MASK, 0xF, false));
+}
+
+// Maximum of an unsigned 32-bit value over the 64 lanes, returned to every
+// lane.  Inclusive prefix maxima within each row of 16 lanes (row_shr 1, 2,
+// 4, 8), then row 0's maximum into row 1 and row 2's into row 3 (row_bcast
+// 15), then row 1's into rows 2-3 (row_bcast 31): lane 63 ends with the
+// maximum of all lanes.
+__device__ __forceinline__ uint32_t wave_max32(uint32_t v) {
+    v = max(v, dpp32<0x111, 0xF>(v));
+    v = max(v, dpp32<0x112, 0xF>(v));
+    v = max(v, dpp32<0x114, 0xF>(v));
+    v = max(v, dpp32<0x118, 0xF>(v));
+    v = max(v, dpp32<0x142, 0xA>(v));
+    v = max(v, dpp32<0x143, 0xC>(v));
+    return static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), 63));
+}
+
+// Maximum of a 64-bit key over the wave: the largest high word first, then
+// the largest low word among the lanes that hold it (two 32-bit reductions
+// are shorter dependent chains than one on 64-bit values).
+__device__ __forceinline__ uint64_t wave_max64(uint64_t v) {
+    const uint32_t hi = wave_max32(static_cast<uint32_t>(v >> 32));
+    const uint32_t lo = wave_max32(static_cast<uint32_t>(v >> 32) == hi ? static_cast<uint32_t>(v) : 0u);
     return (static_cast<uint64_t>(hi) << 32) | lo;
 }
 
-// Maximum over the 64 lanes, returned to every lane.  Inclusive prefix
-// maxima within each row of 16 lanes (row_shr 1, 2, 4, 8), then row 0's
-// maximum into row 1 and row 2's into row 3 (row_bcast 15), then row 1's into
-// rows 2-3 (row_bcast 31): lane 63 ends with the maximum of all lanes.
-__device__ __forceinline__ uint64_t wave_max64(uint64_t v) {
-    v = umax64(v, dpp64<0x111, 0xF>(v));
-    v = umax64(v, dpp64<0x112, 0xF>(v));
-    v = umax64(v, dpp64<0x114, 0xF>(v));
-    v = umax64(v, dpp64<0x118, 0xF>(v));
-    v = umax64(v, dpp64<0x142, 0xA>(v));
-    v = umax64(v, dpp64<0x143, 0xC>(v));
-    const uint32_t lo = __builtin_amdgcn_readlane(static_cast<int>(static_cast<uint32_t>(v)), 63);
-    const uint32_t hi = __builtin_amdgcn_readlane(static_cast<int>(static_cast<uint32_t>(v >> 32)), 63);
-    return (static_cast<uint64_t>(hi) << 32) | lo;
+// Largest of the NK keys below `bound` (0 if none), as a balanced tree.
+template <int NK>
+__device__ __forceinline__ uint64_t masked_max(const uint64_t (&key)[NK], uint64_t bound) {
+    uint64_t t[NK];
+#pragma unroll
+    for (int i = 0; i < NK; ++i) t[i] = key[i] < bound ? key[i] : 0ull;
+#pragma unroll
+    for (int w = 1; w < NK; w *= 2)
+#pragma unroll
+        for (int i = 0; i + w < NK; i += 2 * w) t[i] = umax64(t[i], t[i + w]);
+    return t[0];
 }
 
 // k rounds over NK keys per lane held in registers; lane r writes the
-// round-r winner to out[r] (r < k).
+// round-r winner to out[r] (r < k): the k largest keys, largest first.
 template <int NK>
 __device__ __forceinline__ void wave_select(const uint64_t (&key)[NK], int k, uint64_t* out) {
     const int lane = threadIdx.x & (kWave - 1);
     uint64_t bound = ~0ull;
     for (int r = 0; r < k; ++r) {
-        uint64_t best = 0ull;
-#pragma unroll
-        for (int i = 0; i < NK; ++i)
-            if (key[i] < bound) best = umax64(best, key[i]);
-        best = wave_max64(best);
-        if (lane == (r & (kWave - 1))) out[r] = best;
+        const uint64_t best = wave_max64(masked_max(key, bound));
+        if (lane == r) out[r] = best;
         bound = best;
     }
 }
 
+template <int KPL>
 __global__ __launch_bounds__(kBlockThreads)
 void topk_chunk_kernel(const float* __restrict__ y, int64_t N, int k, int nwchunks,
                        uint64_t* __restrict__ cand) {
@@ -97,79 +116,118 @@ void topk_chunk_kernel(const float* __restrict__ y, int64_t N, int k, int nwchun
     if (c >= nwchunks) return;                                        // whole wave leaves together
     const int lane = threadIdx.x & (kWave - 1);
     const float* ym = y + static_cast<int64_t>(m) * N;
-    uint64_t key[kPerLane];
+    uint64_t key[KPL];
 #pragma unroll
-    for (int i = 0; i < kPerLane; ++i) {
-        const int64_t idx = static_cast<int64_t>(c) * kChunk + i * kWave + lane;
+    for (int i = 0; i < KPL; ++i) {
+        const int64_t idx = (static_cast<int64_t>(c) * KPL + i) * kWave + lane;
         key[i] = idx < N ? order_key(ym[idx], static_cast<uint32_t>(idx)) : 0ull;
     }
     wave_select(key, k, cand + (static_cast<int64_t>(m) * nwchunks + c) * k);
 }
 
+// Tournament over nlists <= 1024 sorted lists of k keys.
 __global__ __launch_bounds__(kMergeThreads)
-void topk_merge_kernel(const float* __restrict__ y, int64_t N, int k, int nwchunks, float softcap,
-                       const uint64_t* __restrict__ cand, float* __restrict__ top_val,
-                       int32_t* __restrict__ top_idx) {
+void topk_tournament_kernel(const float* __restrict__ y, int64_t N, int k, int nlists, float softcap,
+                            const uint64_t* __restrict__ cand, float* __restrict__ top_val,
+                            int32_t* __restrict__ top_idx) {
+    __shared__ uint64_t wbest[kMergeWaves];
+    __shared__ uint64_t won[64];
+    const int m = blockIdx.x;
+    const int t = threadIdx.x;
+    const int w = t / kWave;
+    const int lane = t & (kWave - 1);
+    const uint64_t* list = cand + (static_cast<int64_t>(m) * nlists + t) * k;
+    const bool mine = t < nlists;
+    uint64_t buf[kListRegs];
+#pragma unroll
+    for (int i = 0; i < kListRegs; ++i) buf[i] = (mine && i < k) ? list[i] : 0ull;
+    int next = kListRegs;  // next entry of the list to fetch
+    for (int r = 0; r < k; ++r) {
+        const uint64_t wb = wave_max64(buf[0]);
+        if (lane == 0) wbest[w] = wb;
+        __syncthreads();
+        uint64_t g = lane < kMergeWaves ? wbest[lane] : 0ull;
+        g = wave_max64(g);
+        if (t == 0) won[r] = g;
+        __syncthreads();  // wbest is rewritten next round
+        if (buf[0] == g && g != 0ull) {  // keys are unique: one thread
+#pragma unroll
+            for (int i = 0; i + 1 < kListRegs; ++i) buf[i] = buf[i + 1];
+            buf[kListRegs - 1] = (next < k) ? list[next] : 0ull;
+            ++next;
+        }
+    }
+    __syncthreads();
+    if (t < k) {
+        // k <= N guarantees a real key every round; a zero key would mean
+        // "nothing left" and is never dereferenced.
+        const uint64_t g = won[t];
+        const uint32_t idx = 0xFFFFFFFFu - static_cast<uint32_t>(g);
+        const bool real = g != 0ull && idx < static_cast<uint64_t>(N);
+        const float v = real ? y[static_cast<int64_t>(m) * N + idx] : __builtin_nanf("");
+        top_idx[static_cast<int64_t>(m) * k + t] = real ? static_cast<int32_t>(idx) : -1;
+        top_val[static_cast<int64_t>(m) * k + t] = softcap * tanhf(v / softcap);
+    }
+}
+
+// More than 1024 lists: every wave scans its share of the candidates from
+// memory each round; wave 0 then selects among the waves' winners.
+__global__ __launch_bounds__(kMergeThreads)
+void topk_merge_scan_kernel(const float* __restrict__ y, int64_t N, int k, int nlists, float softcap,
+                            const uint64_t* __restrict__ cand, float* __restrict__ top_val,
+                            int32_t* __restrict__ top_idx) {
     __shared__ uint64_t stage[kMergeWaves * 64];
     const int m = blockIdx.x;
     const int w = threadIdx.x / kWave;
     const int lane = threadIdx.x & (kWave - 1);
-    const int64_t ncand = static_cast<int64_t>(nwchunks) * k;
+    const int64_t ncand = static_cast<int64_t>(nlists) * k;
     const uint64_t* cm = cand + static_cast<int64_t>(m) * ncand;
-    // wave w owns candidates [lo, hi)
     const int64_t per = (ncand + kMergeWaves - 1) / kMergeWaves;
     const int64_t lo = w * per;
     const int64_t hi = (lo + per < ncand) ? lo + per : ncand;
-    if (per <= static_cast<int64_t>(kWave) * kMergeRegs) {
-        uint64_t key[kMergeRegs];
-#pragma unroll
-        for (int i = 0; i < kMergeRegs; ++i) {
-            const int64_t j = lo + i * kWave + lane;
-            key[i] = j < hi ? cm[j] : 0ull;
+    uint64_t bound = ~0ull;
+    for (int r = 0; r < k; ++r) {
+        uint64_t best = 0ull;
+        for (int64_t j = lo + lane; j < hi; j += kWave) {
+            const uint64_t v = cm[j];
+            if (v < bound) best = umax64(best, v);
         }
-        wave_select(key, k, stage + w * 64);
-    } else {
-        // very large N: scan this wave's share from memory every round
-        uint64_t bound = ~0ull;
-        for (int r = 0; r < k; ++r) {
-            uint64_t best = 0ull;
-            for (int64_t j = lo + lane; j < hi; j += kWave) {
-                const uint64_t v = cm[j];
-                if (v < bound) best = umax64(best, v);
-            }
-            best = wave_max64(best);
-            if (lane == r) stage[w * 64 + r] = best;
-            bound = best;
-        }
+        best = wave_max64(best);
+        if (lane == r) stage[w * 64 + r] = best;
+        bound = best;
     }
     __syncthreads();
     if (w == 0) {
-        // k <= 64 winners per wave, 16 waves: 16 keys per lane
         uint64_t key[kMergeWaves];
 #pragma unroll
         for (int i = 0; i < kMergeWaves; ++i) key[i] = lane < k ? stage[i * 64 + lane] : 0ull;
-        uint64_t bound = ~0ull;
+        uint64_t b2 = ~0ull;
         for (int r = 0; r < k; ++r) {
-            uint64_t best = 0ull;
-#pragma unroll
-            for (int i = 0; i < kMergeWaves; ++i)
-                if (key[i] < bound) best = umax64(best, key[i]);
-            best = wave_max64(best);
+            const uint64_t best = wave_max64(masked_max(key, b2));
             if (lane == 0) {
-                // k <= N guarantees a real key every round; a zero key would
-                // mean "nothing left" and is never dereferenced.
                 const uint32_t idx = 0xFFFFFFFFu - static_cast<uint32_t>(best);
                 const bool real = best != 0ull && idx < static_cast<uint64_t>(N);
                 const float v = real ? y[static_cast<int64_t>(m) * N + idx] : __builtin_nanf("");
                 top_idx[static_cast<int64_t>(m) * k + r] = real ? static_cast<int32_t>(idx) : -1;
                 top_val[static_cast<int64_t>(m) * k + r] = softcap * tanhf(v / softcap);
             }
-            bound = best;
+            b2 = best;
         }
     }
 }
 
-int64_t wave_chunks_of(int64_t N) { return (N + kChunk - 1) / kChunk; }
+// Keys per lane of stage 1: the smallest of 4, 16, 64 that leaves at most
+// 1024 chunks (64 for longer rows).
+int keys_per_lane(int64_t N) {
+    if (N <= int64_t{kMaxLists} * kWave * 4) return 4;
+    if (N <= int64_t{kMaxLists} * kWave * 16) return 16;
+    return 64;
+}
+
+int64_t wave_chunks_of(int64_t N) {
+    const int64_t chunk = static_cast<int64_t>(kWave) * keys_per_lane(N);
+    return (N + chunk - 1) / chunk;
+}
 
 size_t align256(size_t b) { return (b + 255) & ~static_cast<size_t>(255); }
 
@@ -188,12 +246,27 @@ hipError_t launch_topk(const float* y, float* top_val, int32_t* top_idx, int64_t
     uint64_t* cand = reinterpret_cast<uint64_t*>(
         static_cast<char*>(ws) + align256(static_cast<size_t>(N) * static_cast<size_t>(M) * sizeof(float)));
     const unsigned blocks = static_cast<unsigned>((nwchunks + kWavesPerBlock - 1) / kWavesPerBlock);
-    hipLaunchKernelGGL(topk_chunk_kernel, dim3(blocks, static_cast<unsigned>(M)), dim3(kBlockThreads), 0, stream,
-                       y, N, k, nwchunks, cand);
+    const dim3 grid(blocks, static_cast<unsigned>(M));
+    switch (keys_per_lane(N)) {
+    case 4:
+        hipLaunchKernelGGL(topk_chunk_kernel<4>, grid, dim3(kBlockThreads), 0, stream, y, N, k, nwchunks, cand);
+        break;
+    case 16:
+        hipLaunchKernelGGL(topk_chunk_kernel<16>, grid, dim3(kBlockThreads), 0, stream, y, N, k, nwchunks, cand);
+        break;
+    default:
+        hipLaunchKernelGGL(topk_chunk_kernel<64>, grid, dim3(kBlockThreads), 0, stream, y, N, k, nwchunks, cand);
+        break;
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(topk_merge_kernel, dim3(static_cast<unsigned>(M)), dim3(kMergeThreads), 0, stream,
-                       y, N, k, nwchunks, softcap, cand, top_val, top_idx);
+    if (nwchunks <= kMaxLists) {
+        hipLaunchKernelGGL(topk_tournament_kernel, dim3(static_cast<unsigned>(M)), dim3(kMergeThreads), 0, stream,
+                           y, N, k, nwchunks, softcap, cand, top_val, top_idx);
+    } else {
+        hipLaunchKernelGGL(topk_merge_scan_kernel, dim3(static_cast<unsigned>(M)), dim3(kMergeThreads), 0, stream,
+                           y, N, k, nwchunks, softcap, cand, top_val, top_idx);
+    }
     return hipGetLastError();
 }
 

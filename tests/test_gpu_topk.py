@@ -126,3 +126,41 @@ def test_nan_inf_and_signed_zero_order():
     v = host(vals)[0]
     assert v[0] == np.float32(30.0 * np.tanh(1.0 / 30.0)) or abs(v[0] - 30 * np.tanh(1 / 30)) < 1e-6
     assert v[3] == -30.0 and np.isnan(v[4]) and np.isnan(v[5])
+
+
+def _topk_f32(y, k):
+    qmv = _qmv()
+    import torch
+    M, N = y.shape
+    wsb = qmv.logits_topk_ws_bytes(N, M, k)
+    ws = torch.empty(wsb, dtype=torch.uint8, device="cuda:0")
+    vals = empty((M, k))
+    idx = empty((M, k), dtype=torch.int32)
+    qmv.qmvdbg_topk_f32(dev(y), vals, idx, N, M, k, 30.0, ws, wsb)
+    return host(vals), host(idx)
+
+
+# Row lengths around the stage-1 chunk-size steps (4, 16 and 64 keys per lane)
+# and past 1024 chunks of 4096 (the rescanning merge).
+@pytest.mark.parametrize("N,k", [(262144, 10), (262145, 64), (1048576, 7), (1048577, 10), (4194305, 10)])
+def test_topk_long_rows(N, k):
+    say(f"qmvdbg_topk_f32 N={N} k={k}")
+    rng = np.random.default_rng(N % 1000 + k)
+    y = rng.standard_normal((2, N)).astype(np.float32)
+    y[1, rng.choice(N, 1000, replace=False)] = np.float32(2.5)  # many exact ties
+    vals, idx = _topk_f32(y, k)
+    for m in range(2):
+        ref = oracle.topk(y[m].astype(np.float64), k)
+        assert idx[m].tolist() == ref.tolist(), f"m={m}"
+        zr = oracle.softcap(y[m, ref].astype(np.float64), 30.0)
+        assert np.all(np.abs(vals[m] - zr) <= 1e-5)
+
+
+@pytest.mark.parametrize("N", [5000, 300000, 2000000])
+def test_topk_one_chunk_holds_every_winner(N):
+    # A decreasing row puts the k largest values in the first chunk, so one
+    # list of the merge supplies every winner (more than it keeps in registers).
+    say(f"qmvdbg_topk_f32 decreasing row N={N}")
+    y = (np.arange(N, 0, -1, dtype=np.float64) * 1e-3).astype(np.float32)[None, :]
+    vals, idx = _topk_f32(y, 64)
+    assert idx[0].tolist() == oracle.topk(y[0].astype(np.float64), 64).tolist()
