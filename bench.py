@@ -37,8 +37,8 @@ sys.path.insert(0, ROOT)
 TRAFFIC_PROFILE = os.path.join("profiles", "qmv_bench_workloads_hbm_traffic.md")
 # kernel symbol and workgroup count of each timed launch at N=21504, K=5376
 KERNEL_OF = {
-    "qmv_q4_0": ("qmv::gemv_unit_kernel<0, 2, false>", 896),
-    "qmv_q4_0_geglu": ("qmv::gemv_unit_kernel<0, 1, true>", 1792),
+    "qmv_q4_0": ("qmv::gemv_unit_kernel<0, 1, false>", 1024),
+    "qmv_q4_0_geglu": ("qmv::gemv_unit_kernel<0, 1, true>", 1024),
 }
 
 

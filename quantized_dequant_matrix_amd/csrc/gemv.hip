@@ -162,13 +162,15 @@ __device__ __forceinline__ void stage_x(float* xs, const float* __restrict__ x, 
             }
         }
     } else {
+        // unaligned x: 4 scalar loads in flight per thread (few registers:
+        // the weights of the first pass are already in flight)
         const int n = G * kUnitElems;
-        for (int base = 0; base < n; base += 16 * kBlockThreads) {
-            float v[16];
+        for (int base = 0; base < n; base += 4 * kBlockThreads) {
+            float v[4];
 #pragma unroll
-            for (int j = 0; j < 16; ++j) v[j] = x[min(base + j * kBlockThreads + static_cast<int>(threadIdx.x), n - 1)];
+            for (int j = 0; j < 4; ++j) v[j] = x[min(base + j * kBlockThreads + static_cast<int>(threadIdx.x), n - 1)];
 #pragma unroll
-            for (int j = 0; j < 16; ++j) {
+            for (int j = 0; j < 4; ++j) {
                 const int i = min(base + j * kBlockThreads + static_cast<int>(threadIdx.x), n - 1);
                 xs[(i >> 8) * kXsStride + (i & 255)] = v[j];
             }
@@ -357,7 +359,9 @@ hipError_t launch_unit(const void* W0, const void* W1, const float* x, float* y,
     const int S = kWave / G;
     const int rows_per_pass = S * R;
     const int npasses = (N + rows_per_pass - 1) / rows_per_pass;
-    const int max_blocks = device_cus() * 8;
+    // at most as many workgroups as are resident at once (4 per CU at
+    // <= 128 VGPRs); longer matrices take several passes per wave
+    const int max_blocks = device_cus() * 4;
     int blocks = (npasses + kWavesPerBlock - 1) / kWavesPerBlock;
     if (blocks > max_blocks) blocks = max_blocks;
     const size_t lds = static_cast<size_t>(G) * kXsStride * sizeof(float);
@@ -411,7 +415,7 @@ hipError_t launch_gemv(int fmt, const void* W, const void* W_up, const float* x,
     }
     switch (fmt) {
     case kQ4_0:
-        return unit ? launch_unit<kQ4_0, 2, false>(W, nullptr, x, y, N, G, stream)
+        return unit ? launch_unit<kQ4_0, 1, false>(W, nullptr, x, y, N, G, stream)
                     : launch_generic<kQ4_0, false>(W, nullptr, x, y, N, K, stream);
     case kQ8_0:
         return unit ? launch_unit<kQ8_0, 1, false>(W, nullptr, x, y, N, G, stream)
