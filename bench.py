@@ -282,9 +282,25 @@ def measure_rows(torch, qmv, synth, dev):
                                                      wsb), 20, warm=3)
     b = Wd.numel() + c["K"] * 4 + c["N"] * 4
     res["c3_logits_topk_q8_0_262144x5376_k10"] = {"us": ms * 1e3, "bytes": b, "GB/s": b / ms / 1e6}
+    # gap between the k-th and (k+1)-th logit (the index set is unique when it
+    # exceeds twice the float tolerance); the logits are left in the workspace
+    ylog = ws[: c["N"] * 4].view(torch.float32)
+    top = torch.topk(ylog.double(), k + 1).values
+    res["c3_kth_logit_margin"] = {"value": float(top[k - 1] - top[k]), "seed": synth.SEEDS["c3"]}
     y = torch.empty((1, c["N"]), device=dev)
     ms = _time_loop(torch, lambda i: qmv.qmv_q8_0(Wd, xd, y, c["N"], c["K"], 1), 20, warm=3)
     res["c3_qmv_q8_0_only_262144x5376"] = {"us": ms * 1e3, "bytes": b, "GB/s": b / ms / 1e6}
+    # the two-stage top-k alone, on the same logits
+    yl = ylog.clone().reshape(1, -1)
+    ms = _time_loop(torch, lambda i: qmv.qmvdbg_topk_f32(yl, vals, idx, c["N"], 1, k, c["softcap"], ws, wsb), 50,
+                    warm=3)
+    res["c3_topk_only_262144_k10"] = {"us": ms * 1e3, "bytes": c["N"] * 4, "GB/s": c["N"] * 4 / ms / 1e6}
+    # a plain device-to-device copy of 256 MB (read + write), next to the GEMV rates
+    a = torch.empty(256 * 1000 * 1000, dtype=torch.uint8, device=dev).fill_(1)
+    bb = torch.empty_like(a)
+    ms = _time_loop(torch, lambda i: bb.copy_(a), 20, warm=3)
+    res["copy_256MB_read_plus_write"] = {"us": ms * 1e3, "bytes": 2 * a.numel(), "GB/s": 2 * a.numel() / ms / 1e6}
+    del a, bb
     for v in res.values():
         for key in list(v):
             if isinstance(v[key], float):
@@ -307,12 +323,21 @@ def cpu_baseline(synth, Ws, Wg, Wu, x, N, K, bytes_step, seconds):
         el = time.perf_counter() - t0
         if el >= seconds:
             break
+    cores = oracle.num_threads()
+    # the 4096 x 4096 workload single-threaded, for reference
+    c1W, c1x = synth.config_problem("c1")
+    oracle.set_num_threads(1)
+    t1 = time.perf_counter()
+    oracle.qmv("q4_0", c1W, 4096, 4096, c1x)
+    t1 = time.perf_counter() - t1
+    oracle.set_num_threads(cores)
     return {
         "value": round(bytes_step * reps / el / 1e9, 3),
         "unit": "GB/s",
-        "cores": oracle.num_threads(),
+        "cores": cores,
         "kind": "oracle",
         "sample": f"{reps} whole steps (3 x 21504x5376 Q4_0 matrices each) in {el:.1f} s, float64, OpenMP",
+        "c1_4096x4096_single_thread_s": round(t1, 4),
         "cpu_model": _cpu_model(),
     }
 

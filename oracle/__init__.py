@@ -63,6 +63,7 @@ def _load():
     lib.oracle_qmm_q4_0_q8.argtypes = [P, I64, I64, P, P, I64, P, I64, P, P]
     lib.oracle_topk.argtypes = [P, I64, ctypes.c_int32, P]
     lib.oracle_num_threads.restype = ctypes.c_int
+    lib.oracle_set_num_threads.argtypes = [ctypes.c_int]
     _lib = lib
     return lib
 
@@ -80,6 +81,11 @@ def _rows_arg(rows, N):
 
 def num_threads() -> int:
     return int(_load().oracle_num_threads())
+
+
+def set_num_threads(n: int) -> None:
+    """Thread count of the oracle's OpenMP loops (for timing only)."""
+    _load().oracle_set_num_threads(int(n))
 
 
 def fp16_to_f64(h: int) -> float:

@@ -408,3 +408,12 @@ int oracle_num_threads(void) {
     return 1;
 #endif
 }
+
+/* Thread count of the OpenMP loops (timing the oracle single-threaded). */
+void oracle_set_num_threads(int n) {
+#ifdef _OPENMP
+    if (n > 0) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
