@@ -35,11 +35,19 @@ sys.path.insert(0, ROOT)
 # (FETCH_SIZE / WRITE_SIZE, scaled by a plain copy); it is reported only while
 # the sources it was measured on are unchanged.
 TRAFFIC_PROFILE = os.path.join("profiles", "qmv_bench_workloads_hbm_traffic.md")
-# kernel symbol and workgroup count of each timed launch at N=21504, K=5376
+# kernel symbol of each timed launch, and its workgroups per CU at most
 KERNEL_OF = {
-    "qmv_q4_0": ("qmv::gemv_unit_kernel<0, 1, false>", 1024),
-    "qmv_q4_0_geglu": ("qmv::gemv_unit_kernel<0, 1, true>", 1024),
+    "qmv_q4_0": ("qmv::gemv_unit_kernel<0, 1, false>", 3),
+    "qmv_q4_0_geglu": ("qmv::gemv_unit_kernel<0, 1, true>", 4),
 }
+
+
+def unit_grid(N: int, K: int, cus: int, per_cu: int) -> int:
+    """Workgroups of the unit GEMV launch: 4 waves per workgroup, one pass of
+    64 // (K/256) rows per wave, capped at the resident count."""
+    rows_per_pass = 64 // (K // 256)
+    npasses = -(-N // rows_per_pass)
+    return min(-(-npasses // 4), cus * per_cu)
 
 
 def profiled_traffic(kernel: str, grid: int):
@@ -160,7 +168,8 @@ def main():
     value = bytes_step / (ms_step * 1e-3) / 1e9
     kernels = {}
     for entry, b, tk in (("qmv_q4_0", bytes_single, t_single), ("qmv_q4_0_geglu", bytes_pair, t_pair)):
-        sym, grid = KERNEL_OF[entry]
+        sym, per_cu = KERNEL_OF[entry]
+        grid = unit_grid(N, K, torch.cuda.get_device_properties(dev).multi_processor_count, per_cu)
         kernels[entry] = {"kernel": sym, "workgroups": grid, "bytes": b, "us": round(tk * 1e3, 3),
                           "GB/s": round(b / (tk * 1e-3) / 1e9, 1), "hbm_traffic_bytes": profiled_traffic(sym, grid)}
     dom_entry, dom = max(kernels.items(), key=lambda kv: kv[1]["us"])

@@ -359,9 +359,11 @@ hipError_t launch_unit(const void* W0, const void* W1, const float* x, float* y,
     const int S = kWave / G;
     const int rows_per_pass = S * R;
     const int npasses = (N + rows_per_pass - 1) / rows_per_pass;
-    // at most as many workgroups as are resident at once (4 per CU at
-    // <= 128 VGPRs); longer matrices take several passes per wave
-    const int max_blocks = device_cus() * 4;
+    // At most as many workgroups as are resident at once (4 per CU at
+    // <= 128 VGPRs); longer matrices take several passes per wave.  One
+    // matrix at a time runs best with 3 per CU: a wave's first loads then
+    // share the memory system with fewer others and arrive sooner.
+    const int max_blocks = device_cus() * (PAIR ? 4 : 3);
     int blocks = (npasses + kWavesPerBlock - 1) / kWavesPerBlock;
     if (blocks > max_blocks) blocks = max_blocks;
     const size_t lds = static_cast<size_t>(G) * kXsStride * sizeof(float);
