@@ -32,6 +32,23 @@ def test_every_declared_symbol_is_exported_and_bound():
     assert sorted(qmv.EXPORTS) == names
 
 
+def test_launch_path_allocates_copies_and_waits_for_nothing():
+    """The library is launch-only: among the HIP runtime calls it imports there
+    is no allocation, no copy or fill, no synchronisation and no graph call, so
+    every buffer is the caller's and every call only enqueues work."""
+    import shutil
+    import subprocess
+    nm = shutil.which("nm")
+    if nm is None:
+        pytest.skip("nm (binutils) is not installed")
+    out = subprocess.run([nm, "-D", "--undefined-only", qmv._LIB_PATH], check=True,
+                         capture_output=True, text=True).stdout
+    hip = sorted({ln.split()[-1].split("@")[0] for ln in out.splitlines() if "hip" in ln})
+    assert "hipLaunchKernel" in hip
+    banned = re.compile(r"^hip(Malloc|Free|HostMalloc|HostRegister|Memcpy|Memset|.*Synchronize|Graph|StreamCreate|EventCreate)")
+    assert [h for h in hip if banned.match(h)] == [], hip
+
+
 def test_status_strings():
     for s in range(7):
         assert qmv.status_str(s)
