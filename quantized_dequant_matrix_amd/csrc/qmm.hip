@@ -11,10 +11,12 @@
 // products as 16 (q_w - 8) in a signed byte, so the sums are 16 isum exactly
 // (|16 isum| <= 32*128*127) and the shift back is exact.
 //   M == 1: qmm_dot_kernel, v_dot4_i32_i8 per lane (an HBM-bound GEMV).
-//   M >= 2: qmm_mfma_kernel, where the work is a dense int8 contraction: one
-//           v_mfma_i32_16x16x32_i8 covers exactly one block (K = 32) of a
-//           16 x 16 tile of (m, n), so every block sum stays exact and gets
-//           its own scale in the float epilogue.
+//   M >= 2: the work is a dense int8 contraction: one v_mfma_i32_16x16x32_i8
+//           covers exactly one block (K = 32) of a 16 x 16 tile of (m, n), so
+//           every block sum stays exact and gets its own scale in the float
+//           epilogue.  qmm_wide_kernel takes the large tilings (M = 512 class),
+//           qmm_mfma_kernel the narrow ones (M = 16 class) and the block-sum
+//           export.
 #include <utility>
 
 #include "qmv_device.h"
@@ -481,6 +483,183 @@ void qmm_mfma_kernel(const uint8_t* __restrict__ W, const int8_t* __restrict__ x
     }
 }
 
+// The wide tiling (M = 512 class), with the weight codes decoded once per
+// workgroup.  A 64 x 64 tile per workgroup, 32 x 32 per wave (2 x 2 MFMA tiles
+// of 16 x 16).  Per chunk of KC = 16 blocks:
+//   * weights: a thread owns 4 whole blocks (72 bytes) of one of the 64 rows,
+//     fetched with 8-byte loads one chunk ahead, decoded in registers to
+//     16 (q - 8) signed bytes and d / 16, and stored in LDS in the MFMA
+//     operand layout: block j, k-group g, row r at
+//     bq[j * kBlockStride + g * kGroupStride + 2 r] (8 bytes).  The group
+//     stride puts a wave's four k-group reads on bank halves two by two, the
+//     block stride puts the four quarter-row writers of a wave on disjoint
+//     banks;
+//   * activations: read from the fragment layout in global memory (the
+//     whole [M, K] set stays in the caches), one block pair ahead of the
+//     multiplies, with unconditional loads so that no branch merges the
+//     waits (the pair after the last one re-reads the last pair).
+template <int KC>
+__global__ __launch_bounds__(kBlockThreads)
+void qmm_wide_kernel(const uint8_t* __restrict__ W, const int8_t* __restrict__ xa, const float* __restrict__ xd,
+                     float* __restrict__ out, int N, int64_t M, int nb, int64_t tm0, int64_t tiles_m, int tiles_n,
+                     int64_t nwg) {
+    constexpr int MW = 2, NW = 2, WM = 2, WN = 2;
+    constexpr int TN = 16 * NW * WN;           // 64 weight rows
+    constexpr int kGroupStride = 2 * TN + 32;  // dwords: k-groups 32 banks apart
+    constexpr int kBlockStride = 4 * kGroupStride + 4;
+    static_assert(TN * 4 == kBlockThreads, "a thread owns one quarter of a row's chunk");
+    static_assert(KC == 16, "four quarters of four blocks per row");
+    static_assert(WM * WN == kWavesPerBlock, "four waves per workgroup");
+    __shared__ __align__(16) uint32_t bq[KC * kBlockStride];
+    __shared__ float bs[KC * TN];
+
+    // Each XCD gets a contiguous run of tiles (same weight rows, all m-tiles).
+    int64_t lin = blockIdx.x;
+    if (nwg % 8 == 0) lin = (lin % 8) * (nwg / 8) + lin / 8;
+    const int64_t tm = tm0 + lin % tiles_m;
+    const int tn = static_cast<int>(lin / tiles_m);
+    const int n0 = tn * TN;
+    const int64_t row_bytes = static_cast<int64_t>(nb) * 18;
+
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wn = w % WN;
+    const int wm = w / WN;
+    const int li = lane & 15;
+    const int lg = lane >> 4;
+
+    // Weight chunk: thread -> row fr, quarter fq = blocks 4 fq .. 4 fq + 3.
+    // nb is a multiple of 8, so a quarter is either whole or past the end;
+    // quarters past the end (and rows past N) read valid bytes that are never
+    // used.  Rows are 16-byte aligned (nb * 18 = 144 * (nb / 8)).
+    const int fr = threadIdx.x >> 2;
+    const int fq = threadIdx.x & 3;
+    const uint8_t* frow = W + static_cast<int64_t>(min(n0 + fr, N - 1)) * row_bytes;
+    uint2 raw[9];
+    auto fetch = [&](int c0) {
+        const int b0 = c0 + 4 * fq;
+        const int64_t off = (b0 < nb) ? static_cast<int64_t>(b0) * 18 : 0;
+        const uint2* src = reinterpret_cast<const uint2*>(frow + off);
+#pragma unroll
+        for (int i = 0; i < 9; ++i) raw[i] = src[i];
+    };
+    auto stash = [&]() {
+        uint32_t dw[18];
+#pragma unroll
+        for (int i = 0; i < 9; ++i) {
+            dw[2 * i] = raw[i].x;
+            dw[2 * i + 1] = raw[i].y;
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int blk = 4 * fq + j;
+            uint32_t dbits, code[4];
+            if ((j & 1) == 0) {  // block starts on a dword: codes 2 bytes in
+                const int q0 = (18 * j) / 4;
+                dbits = dw[q0] & 0xffffu;
+#pragma unroll
+                for (int g = 0; g < 4; ++g) code[g] = __builtin_amdgcn_alignbyte(dw[q0 + g + 1], dw[q0 + g], 2);
+            } else {  // block starts 2 bytes into a dword: codes aligned
+                const int q0 = (18 * j - 2) / 4;
+                dbits = dw[q0] >> 16;
+#pragma unroll
+                for (int g = 0; g < 4; ++g) code[g] = dw[q0 + 1 + g];
+            }
+            uint32_t* dst = bq + blk * kBlockStride + 2 * fr;
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const uint64_t v = q4_codes_to_s8(code[g]);
+                *reinterpret_cast<uint2*>(dst + g * kGroupStride) =
+                    make_uint2(static_cast<uint32_t>(v), static_cast<uint32_t>(v >> 32));
+            }
+            bs[blk * TN + fr] = half_bits_to_float(dbits) * 0.0625f;
+        }
+    };
+
+    struct AFrag {
+        uint64_t e[MW], o[MW];      // codes of blocks b, b + 1
+        float xe[MW][4], xo[MW][4];  // their scales, rows 4 lg .. 4 lg + 3
+    };
+    auto load_a = [&](int64_t b, AFrag& A) {
+#pragma unroll
+        for (int mi = 0; mi < MW; ++mi) {
+            const int64_t mt = tm * (MW * WM) + wm * MW + mi;
+            const uint4 v = *reinterpret_cast<const uint4*>(xa + ((mt * (nb >> 1) + (b >> 1)) * kWave + lane) * 16);
+            A.e[mi] = static_cast<uint64_t>(v.x) | (static_cast<uint64_t>(v.y) << 32);
+            A.o[mi] = static_cast<uint64_t>(v.z) | (static_cast<uint64_t>(v.w) << 32);
+            const float4 de = *reinterpret_cast<const float4*>(xd + (mt * nb + b) * 16 + 4 * lg);
+            const float4 dq = *reinterpret_cast<const float4*>(xd + (mt * nb + b + 1) * 16 + 4 * lg);
+            A.xe[mi][0] = de.x; A.xe[mi][1] = de.y; A.xe[mi][2] = de.z; A.xe[mi][3] = de.w;
+            A.xo[mi][0] = dq.x; A.xo[mi][1] = dq.y; A.xo[mi][2] = dq.z; A.xo[mi][3] = dq.w;
+        }
+    };
+
+    float acc[MW][NW][4];
+#pragma unroll
+    for (int mi = 0; mi < MW; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < NW; ++ni)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) acc[mi][ni][r] = 0.0f;
+
+    // block pair jp of the chunk in LDS, activations from A
+    auto mul_pair = [&](int jp, const AFrag& A) {
+        const int je = 2 * jp, jo = 2 * jp + 1;
+#pragma unroll
+        for (int ni = 0; ni < NW; ++ni) {
+            const int r = (wn * NW + ni) * 16 + li;
+            const uint2 be2 = *reinterpret_cast<const uint2*>(bq + je * kBlockStride + lg * kGroupStride + 2 * r);
+            const uint2 bo2 = *reinterpret_cast<const uint2*>(bq + jo * kBlockStride + lg * kGroupStride + 2 * r);
+            const float se = bs[je * TN + r];
+            const float so = bs[jo * TN + r];
+            const uint64_t be = static_cast<uint64_t>(be2.x) | (static_cast<uint64_t>(be2.y) << 32);
+            const uint64_t bo = static_cast<uint64_t>(bo2.x) | (static_cast<uint64_t>(bo2.y) << 32);
+#pragma unroll
+            for (int mi = 0; mi < MW; ++mi) {
+                const v4i zero = {0, 0, 0, 0};
+                const v4i De = __builtin_amdgcn_mfma_i32_16x16x32_i8(static_cast<long>(A.e[mi]), static_cast<long>(be),
+                                                                      zero, 0, 0, 0);
+                const v4i Do = __builtin_amdgcn_mfma_i32_16x16x32_i8(static_cast<long>(A.o[mi]), static_cast<long>(bo),
+                                                                      zero, 0, 0, 0);
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    acc[mi][ni][q] = fmaf(static_cast<float>(De[q]), se * A.xe[mi][q], acc[mi][ni][q]);
+                    acc[mi][ni][q] = fmaf(static_cast<float>(Do[q]), so * A.xo[mi][q], acc[mi][ni][q]);
+                }
+            }
+        }
+    };
+
+    AFrag A0, A1;
+    load_a(0, A0);
+    fetch(0);
+    for (int c0 = 0; c0 < nb; c0 += KC) {
+        __syncthreads();  // every wave is done with the previous chunk
+        stash();
+        __syncthreads();
+        if (c0 + KC < nb) fetch(c0 + KC);
+        const int npair = min(KC, nb - c0) >> 1;  // 4 or 8: even
+        for (int jp = 0; jp < npair; jp += 2) {
+            load_a(c0 + 2 * jp + 2, A1);
+            mul_pair(jp, A0);
+            const int64_t nxt = c0 + 2 * jp + 4;
+            load_a(nxt < nb ? nxt : nb - 2, A0);
+            mul_pair(jp + 1, A1);
+        }
+    }
+#pragma unroll
+    for (int mi = 0; mi < MW; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < NW; ++ni) {
+            const int n = n0 + (wn * NW + ni) * 16 + li;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int64_t m = (tm * (MW * WM) + wm * MW + mi) * 16 + 4 * lg + q;
+                if (m < M && n < N) out[m * N + n] = acc[mi][ni][q];
+            }
+        }
+}
+
 // y = sum over K splits of the partial sums, in split order.
 __global__ __launch_bounds__(kBlockThreads)
 void qmm_reduce_kernel(const float* __restrict__ P, float* __restrict__ y, int ks, int64_t MN) {
@@ -590,6 +769,24 @@ hipError_t launch_mfma(const QmmPlan& p, const void* W, const int8_t* xa, const 
     return hipSuccess;
 }
 
+// The wide path: qmm_wide_kernel over all tiles, in slices of m-tiles that
+// keep the grid within 2^30 workgroups.
+hipError_t launch_wide(const QmmPlan& p, const void* W, const int8_t* xa, const float* xd, float* y, int64_t N,
+                       int64_t K, int64_t M, hipStream_t stream) {
+    int64_t mt_slice = (int64_t{1} << 30) / p.tiles_n;
+    mt_slice = mt_slice < p.tiles_m ? mt_slice : p.tiles_m;
+    for (int64_t tm0 = 0; tm0 < p.tiles_m; tm0 += mt_slice) {
+        const int64_t tms = (p.tiles_m - tm0 < mt_slice) ? p.tiles_m - tm0 : mt_slice;
+        const int64_t nwg = tms * p.tiles_n;
+        hipLaunchKernelGGL((qmm_wide_kernel<16>), dim3(static_cast<unsigned>(nwg)), dim3(kBlockThreads), 0, stream,
+                           static_cast<const uint8_t*>(W), xa, xd, y, static_cast<int>(N), M, static_cast<int>(K / 32),
+                           tm0, tms, p.tiles_n, nwg);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
 // The M == 1 and K % 256 != 0 paths (row-major activation codes).
 hipError_t launch_dot(const QmmPlan& p, const void* W, const int8_t* qx, const float* dx, float* y, int32_t* isum,
                       int64_t N64, int64_t K, int64_t M, hipStream_t stream) {
@@ -654,7 +851,7 @@ hipError_t launch_qmm_q8act(const void* W, const float* x, float* y, int64_t N, 
                         : launch_quantize<false>(x, q, d, K, M, M, stream);
     if (e != hipSuccess) return e;
     if (!mfma) return launch_dot(p, W, q, d, y, nullptr, N, K, M, stream);
-    if (p.path == kPathWide) return launch_mfma<QMM_WIDE, kModeY>(p, W, q, d, y, nullptr, N, K, M, stream);
+    if (p.path == kPathWide) return launch_wide(p, W, q, d, y, N, K, M, stream);
     if (p.ks == 1) return launch_mfma<QMM_NARROW, kModeY>(p, W, q, d, y, nullptr, N, K, M, stream);
     e = launch_mfma<QMM_NARROW, kModePartial>(p, W, q, d, part, nullptr, N, K, M, stream);
     if (e != hipSuccess) return e;

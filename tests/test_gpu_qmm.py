@@ -117,6 +117,20 @@ def test_qmm_workload_m512_sampled():
     say(f"c4 M=512: worst err/tol {w:.3g}")
 
 
+def test_qmm_wide_ragged_sampled():
+    """The wide tiling with N and M off the 64-row tiles and a half-full last
+    weight chunk (K / 32 = 24 blocks: one chunk of 16, one of 8)."""
+    N, K, M = 8200, 768, 520
+    say(f"qmm_q4_0_q8act wide tiling N={N} K={K} M={M}, sampled rows")
+    W, x = synth.problem("q4_0", N, K, M, 77)
+    y = gpu_qmm(W, x, N, K, M)
+    rows = np.unique(np.concatenate([[0, 63, 64, 8191, 8192, N - 1],
+                                     np.random.default_rng(5).choice(N, 40, replace=False)]))
+    yr, S = _qmm_ref(W, x, N, K, M, rows=rows)
+    assert_within(y[:, rows], yr, oracle.float_tol(S), "wide ragged")
+    assert np.all(np.isfinite(y))
+
+
 @pytest.mark.parametrize("N,K,M", [(1, 32, 1), (9, 96, 2), (65, 256, 5), (200, 5376, 17), (31, 16640, 3)])
 def test_qmm_shapes(N, K, M):
     say(f"qmm_q4_0_q8act N={N} K={K} M={M}")
