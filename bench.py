@@ -277,6 +277,27 @@ def measure_rows(torch, qmv, synth, dev):
                                           "int_TOPS": 2.0 * M * N * K / ms / 1e9}
     del slots
 
+    # Q4_0 x float32 activations, a few rows at once, on the 21504 x 5376 FFN
+    # matrix (8 slots): the fixed-eight verifier batch and the 32-row prefill
+    # tile, next to the same rows through the matrix-vector kernel row by row
+    c = synth.CONFIGS["c2"]
+    N, K = c["N"], c["K"]
+    W, _ = synth.config_problem("c2")
+    slots = [t(W) for _ in range(8)]
+    for M in (8, 32):
+        x = synth.activations(M, K, 2100 + M)
+        xd, y = t(x), torch.empty((M, N), device=dev)
+        wsb = qmv.qmm_q4_0_f32act_ws_bytes(N, K, M)
+        ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
+        ms = _time_loop(torch, lambda i: qmv.qmm_q4_0_f32act(slots[i % 8], xd, y, N, K, M, ws, wsb), 100, warm=3)
+        b = W.nbytes + M * K * 4 + M * N * 4
+        res[f"c2_qmm_q4_0_f32act_M{M}"] = {"us": ms * 1e3, "bytes": b, "GB/s": b / ms / 1e6,
+                                           "TFLOPS": 2.0 * M * N * K / ms / 1e9}
+        if M == 8:
+            ms = _time_loop(torch, lambda i: qmv.qmv_q4_0(slots[i % 8], xd, y, N, K, M), 30, warm=2)
+            res["c2_qmv_q4_0_rowwise_M8"] = {"us": ms * 1e3, "bytes": b, "GB/s": b / ms / 1e6}
+    del slots
+
     # C3: Q8_0 262144 x 5376 + soft-cap + top-10 (1.5 GB: one copy streams)
     c = synth.CONFIGS["c3"]
     W, x = synth.config_problem("c3")

@@ -122,6 +122,30 @@ int qmm_q4_0_q8act(const void* W, const float* x, float* y,
                    int64_t N, int64_t K, int64_t M,
                    void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* Q4_0 weights times float32 activations for a few rows at once (small M:
+ * the fixed-eight verifier batch and the 32-row prefill tile), reading the
+ * weights once for all rows.  y float32 [M][N] = sum_k w[n][k] x[m][k], to
+ * the same float32 accuracy as qmv_q4_0; the activations are NOT quantized.
+ * Method: every 32-element block of a row is scaled by a power of two s
+ * (its largest magnitude into [2^14, 2^15)) and split into two float16
+ * terms hi + lo (hi = f16(x / s), lo = f16(x / s - hi)); the block products
+ * (q - 8) * hi and (q - 8) * lo are formed by float16 MFMA with float32
+ * sums and rescaled by d_w * s in float32.  M == 1 and K % 256 != 0 run the
+ * float32 matrix-vector kernels row by row instead.
+ * Activations must be finite.
+ * [roadmap K3: batched Q4_0 matrix-matrix kernels, the 64 x 32 prefill MMA;
+ *  K5: the fixed-eight Q4_0 verifier; batches below eight used the
+ *  matrix-vector kernel there]
+ * ws: device buffer of at least qmm_q4_0_f32act_ws_bytes(N, K, M) bytes,
+ * 16-byte aligned, contents overwritten.  It holds the split activations
+ * and scales (rows padded to the tile height) and, when K is split across
+ * workgroups, the float32 partial sums.  The size depends on (N, K, M)
+ * only; 0 means an invalid shape. */
+size_t qmm_q4_0_f32act_ws_bytes(int64_t N, int64_t K, int64_t M);
+int qmm_q4_0_f32act(const void* W, const float* x, float* y,
+                    int64_t N, int64_t K, int64_t M,
+                    void* ws, size_t ws_bytes, hipStream_t stream);
+
 /* Logit projection over a Q8_0 tied embedding, soft-cap and top-k.
  *   y[m][n] = sum_k w[n][k] x[m][k]                (float32)
  *   z = softcap * tanh(y / softcap)

@@ -323,7 +323,7 @@ void qmm_mfma_kernel(const uint8_t* __restrict__ W, const int8_t* __restrict__ x
     const int64_t K = static_cast<int64_t>(nb) * 32;
     const int64_t row_bytes = static_cast<int64_t>(nb) * 18;
 
-    const int w = threadIdx.x / kWave;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int lane = threadIdx.x & (kWave - 1);
     const int wk = w % WK;
     const int wn = (w / WK) % WN;
@@ -374,10 +374,13 @@ void qmm_mfma_kernel(const uint8_t* __restrict__ W, const int8_t* __restrict__ x
         __syncthreads();
         if (c0 + KC < kb1) fetch(c0 + KC);
         const int npair = min(KC, kb1 - c0) >> 1;
-        for (int cp = wk; cp < npair; cp += WK) {
-            const int64_t b = c0 + 2 * cp;  // blocks b (even) and b + 1
-            uint64_t ae[MW], ao[MW];
+        struct AFrag {
+            uint64_t e[MW], o[MW];
             float xe[MW][4], xo[MW][4];
+        };
+        // activations of block pair cp of this chunk (blocks b, b + 1)
+        auto load_a = [&](int cp, AFrag& A) {
+            const int64_t b = c0 + 2 * cp;
 #pragma unroll
             for (int mi = 0; mi < MW; ++mi) {
                 const int64_t mt = tm * (MW * WM) + wm * MW + mi;  // 16-row tile
@@ -386,18 +389,21 @@ void qmm_mfma_kernel(const uint8_t* __restrict__ W, const int8_t* __restrict__ x
                     int64_t m = mt * 16 + li;
                     m = m < M ? m : M - 1;
                     const uint32_t* src = reinterpret_cast<const uint32_t*>(xa + m * K + 32 * b);
-                    ae[mi] = static_cast<uint64_t>(src[lg]) | (static_cast<uint64_t>(src[4 + lg]) << 32);
-                    ao[mi] = static_cast<uint64_t>(src[8 + lg]) | (static_cast<uint64_t>(src[12 + lg]) << 32);
+                    A.e[mi] = static_cast<uint64_t>(src[lg]) | (static_cast<uint64_t>(src[4 + lg]) << 32);
+                    A.o[mi] = static_cast<uint64_t>(src[8 + lg]) | (static_cast<uint64_t>(src[12 + lg]) << 32);
                 } else {
                     const uint4 v = *reinterpret_cast<const uint4*>(xa + ((mt * (nb >> 1) + (b >> 1)) * kWave + lane) * 16);
-                    ae[mi] = static_cast<uint64_t>(v.x) | (static_cast<uint64_t>(v.y) << 32);
-                    ao[mi] = static_cast<uint64_t>(v.z) | (static_cast<uint64_t>(v.w) << 32);
+                    A.e[mi] = static_cast<uint64_t>(v.x) | (static_cast<uint64_t>(v.y) << 32);
+                    A.o[mi] = static_cast<uint64_t>(v.z) | (static_cast<uint64_t>(v.w) << 32);
                     const float4 de = *reinterpret_cast<const float4*>(xd + (mt * nb + b) * 16 + 4 * lg);
                     const float4 dq = *reinterpret_cast<const float4*>(xd + (mt * nb + b + 1) * 16 + 4 * lg);
-                    xe[mi][0] = de.x; xe[mi][1] = de.y; xe[mi][2] = de.z; xe[mi][3] = de.w;
-                    xo[mi][0] = dq.x; xo[mi][1] = dq.y; xo[mi][2] = dq.z; xo[mi][3] = dq.w;
+                    A.xe[mi][0] = de.x; A.xe[mi][1] = de.y; A.xe[mi][2] = de.z; A.xe[mi][3] = de.w;
+                    A.xo[mi][0] = dq.x; A.xo[mi][1] = dq.y; A.xo[mi][2] = dq.z; A.xo[mi][3] = dq.w;
                 }
             }
+        };
+        auto mul_pair = [&](int cp, const AFrag& A) {
+            const int64_t b = c0 + 2 * cp;
             uint64_t be[NW], bo[NW];
             float se[NW], so[NW];
 #pragma unroll
@@ -419,9 +425,9 @@ void qmm_mfma_kernel(const uint8_t* __restrict__ W, const int8_t* __restrict__ x
 #pragma unroll
                 for (int ni = 0; ni < NW; ++ni) {
                     const v4i zero = {0, 0, 0, 0};
-                    const v4i De = __builtin_amdgcn_mfma_i32_16x16x32_i8(static_cast<long>(ae[mi]),
+                    const v4i De = __builtin_amdgcn_mfma_i32_16x16x32_i8(static_cast<long>(A.e[mi]),
                                                                           static_cast<long>(be[ni]), zero, 0, 0, 0);
-                    const v4i Do = __builtin_amdgcn_mfma_i32_16x16x32_i8(static_cast<long>(ao[mi]),
+                    const v4i Do = __builtin_amdgcn_mfma_i32_16x16x32_i8(static_cast<long>(A.o[mi]),
                                                                           static_cast<long>(bo[ni]), zero, 0, 0, 0);
                     if constexpr (MODE == kModeISum) {
                         const int n = n0 + (wn * NW + ni) * 16 + li;
@@ -437,11 +443,30 @@ void qmm_mfma_kernel(const uint8_t* __restrict__ W, const int8_t* __restrict__ x
                     } else {
 #pragma unroll
                         for (int r = 0; r < 4; ++r) {
-                            acc[mi][ni][r] = fmaf(static_cast<float>(De[r]), se[ni] * xe[mi][r], acc[mi][ni][r]);
-                            acc[mi][ni][r] = fmaf(static_cast<float>(Do[r]), so[ni] * xo[mi][r], acc[mi][ni][r]);
+                            acc[mi][ni][r] = fmaf(static_cast<float>(De[r]), se[ni] * A.xe[mi][r], acc[mi][ni][r]);
+                            acc[mi][ni][r] = fmaf(static_cast<float>(Do[r]), so[ni] * A.xo[mi][r], acc[mi][ni][r]);
                         }
                     }
                 }
+            }
+        };
+        // This wave's pairs are wk, wk + WK, ...  The activations of the next
+        // one are requested before the current one is multiplied; the loads
+        // are unconditional (past the last pair they re-read the last pair)
+        // so that no branch merges the waits.
+        if (wk < npair) {
+            AFrag A0, A1;
+            int cp = wk;
+            load_a(cp, A0);
+            while (true) {
+                load_a(min(cp + WK, npair - 1), A1);
+                mul_pair(cp, A0);
+                cp += WK;
+                if (cp >= npair) break;
+                load_a(min(cp + WK, npair - 1), A0);
+                mul_pair(cp, A1);
+                cp += WK;
+                if (cp >= npair) break;
             }
         }
     }
@@ -660,6 +685,254 @@ void qmm_wide_kernel(const uint8_t* __restrict__ W, const int8_t* __restrict__ x
         }
 }
 
+// ------------------------------------------------ float32 activations
+// Q4_0 weights times float32 activations for small M (2 .. 32 rows: the
+// fixed-eight verifier and the 32-row prefill tile of ["Gemma 4 M4 Max
+// kernel roadmap", K3 prefill path and K5 advanced candidates]), reading the
+// weights once for all rows.  The activations are not quantized: each
+// 32-element block of a row is scaled by a power of two s = 2^e so that its
+// largest magnitude lies in [2^14, 2^15), and split into two float16 terms,
+// hi = f16(x / s) and lo = f16(x / s - hi).  (q - 8) is exact in float16, so
+// two v_mfma_f32_16x16x32_f16 per block (hi, then lo into the same
+// accumulator) give sum (q - 8) (hi + lo) with exact products and float32
+// sums; |x / s - hi - lo| <= 2^-22 |x / s| for all but float16-subnormal
+// terms, which lie 2^-24 below the block maximum.  The epilogue is
+// y += D * (d_w * s) with d_w the block's float16 scale.
+
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+// Layout of the split activations, Mt = tiles of 16 rows, nb = K / 32:
+//   hl [Mt][nb][64 lanes][32 B]: lane l = i + 16 g holds, for row 16 t + i,
+//      hi then lo of x[4g .. 4g+3] and x[16+4g .. 16+4g+3] of block b (the
+//      elements of code dword g of a Q4_0 block: low nibbles, then high);
+//   sx [Mt][nb][16] float: s of row 16 t + i, block b.
+// Rows M .. 16 Mt - 1 hold zeros (s = 1).
+__global__ __launch_bounds__(kBlockThreads)
+void split_f16_kernel(const float* __restrict__ x, uint8_t* __restrict__ hl, float* __restrict__ sx, int64_t K,
+                      int64_t M, int64_t Mrows, bool vec_x) {
+    const int64_t nb = K / 32;
+    const int64_t total = Mrows * nb;
+    const int t = threadIdx.x & 7;  // elements 4 t .. 4 t + 3 of the block
+    const int64_t stride = static_cast<int64_t>(gridDim.x) * (kBlockThreads / 8);
+    for (int64_t wave_first = (static_cast<int64_t>(blockIdx.x) * kBlockThreads + (threadIdx.x & ~(kWave - 1))) / 8;
+         wave_first < total; wave_first += stride) {
+        const int64_t blk = wave_first + (threadIdx.x & (kWave - 1)) / 8;
+        const bool ok = blk < total;
+        const int64_t m = ok ? blk / nb : 0;
+        const int64_t b = ok ? blk - m * nb : 0;
+        float v[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+        if (ok && m < M) {
+            const float* src = x + m * K + 32 * b + 4 * t;
+            if (vec_x) {
+                const float4 f = *reinterpret_cast<const float4*>(src);
+                v[0] = f.x; v[1] = f.y; v[2] = f.z; v[3] = f.w;
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) v[e] = src[e];
+            }
+        }
+        float a = fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3])));
+#pragma unroll
+        for (int o = 4; o > 0; o >>= 1) a = fmaxf(a, __shfl_xor(a, o, 8));
+        // s = 2^e with a / s in [2^14, 2^15); zero or non-finite blocks keep s = 1
+        const int e = (a > 0.0f && a <= 3.4028234663852886e38f) ? ilogbf(a) - 14 : 0;
+        h2 hi[2], lo[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const float x0 = ldexpf(v[2 * h], -e), x1 = ldexpf(v[2 * h + 1], -e);
+            const _Float16 h0 = static_cast<_Float16>(x0), h1 = static_cast<_Float16>(x1);
+            hi[h] = h2{h0, h1};
+            lo[h] = h2{static_cast<_Float16>(x0 - static_cast<float>(h0)),
+                       static_cast<_Float16>(x1 - static_cast<float>(h1))};
+        }
+        if (ok) {
+            const int64_t mt = m >> 4, i = m & 15;
+            const int g = (t & 3), half = t >> 2;  // elements 4t..: low nibbles (t < 4) or high (t >= 4)
+            uint8_t* dst = hl + (((mt * nb + b) * kWave + i + 16 * g) * 32) + half * 8;
+            *reinterpret_cast<uint2*>(dst) = make_uint2(__builtin_bit_cast(uint32_t, hi[0]), __builtin_bit_cast(uint32_t, hi[1]));
+            *reinterpret_cast<uint2*>(dst + 16) = make_uint2(__builtin_bit_cast(uint32_t, lo[0]), __builtin_bit_cast(uint32_t, lo[1]));
+            if (t == 0) sx[(mt * nb + b) * 16 + i] = ldexpf(1.0f, e);
+        }
+    }
+}
+
+// Code dword c of a Q4_0 block (code bytes 4g .. 4g+3) as the eight float16
+// values (q - 8) in the element order of the split layout.
+__device__ __forceinline__ h8 q4_codes_to_h8(uint32_t c) {
+    const uint32_t p01 = __builtin_amdgcn_perm(0u, c, 0x0c010c00u);  // byte 0 -> bits 0..7, byte 1 -> 16..23
+    const uint32_t p23 = __builtin_amdgcn_perm(0u, c, 0x0c030c02u);  // bytes 2, 3 likewise
+    constexpr uint32_t kNib = 0x000F000Fu, kMagic = 0x64006400u;    // float16 1024 + n
+    const h2 off = {static_cast<_Float16>(1032.0f), static_cast<_Float16>(1032.0f)};
+    const h2 a = __builtin_bit_cast(h2, (p01 & kNib) | kMagic) - off;         // elements 4g, 4g+1
+    const h2 b = __builtin_bit_cast(h2, (p23 & kNib) | kMagic) - off;         // 4g+2, 4g+3
+    const h2 c2 = __builtin_bit_cast(h2, ((p01 >> 4) & kNib) | kMagic) - off;  // 16+4g, 16+4g+1
+    const h2 d = __builtin_bit_cast(h2, ((p23 >> 4) & kNib) | kMagic) - off;   // 16+4g+2, 16+4g+3
+    return h8{a[0], a[1], b[0], b[1], c2[0], c2[1], d[0], d[1]};
+}
+
+// 16 MW rows of m x 16 weight rows per workgroup; the four waves split each
+// chunk's block pairs, their sums are added in LDS in wave order, and K may
+// be split across workgroups (PARTIAL: write split ks of the partial sums).
+// The weight chunk is staged as raw GGUF bytes (16 rows x KC blocks) with
+// 16-byte loads, the next chunk prefetched into registers.
+template <int MW, int KC, bool PARTIAL>
+__global__ __launch_bounds__(kBlockThreads)
+void qmm_f16_kernel(const uint8_t* __restrict__ W, const uint8_t* __restrict__ hl, const float* __restrict__ sx,
+                    float* __restrict__ out, int N, int64_t M, int nb, int64_t tm0, int64_t tiles_m, int tiles_n,
+                    int kb_per, int64_t nwg) {
+    constexpr int TN = 16;
+    constexpr int WK = kWavesPerBlock;
+    constexpr int RB = KC * 18;
+    constexpr int RS = RB + 16;  // LDS row stride: rows 4 banks apart (mod 64)
+    constexpr int PR = RB / 16;
+    constexpr int LPT = TN * PR / kBlockThreads;
+    static_assert(KC % 8 == 0 && TN * PR == LPT * kBlockThreads, "the weight chunk must split evenly");
+    constexpr int NV = MW * 4;
+    static_assert((WK - 1) * NV * kWave <= TN * RS / 4, "the reduction fits the weight tile");
+    __shared__ __align__(16) uint32_t wt[TN * RS / 4];
+
+    int64_t lin = blockIdx.x;
+    if (nwg % 8 == 0) lin = (lin % 8) * (nwg / 8) + lin / 8;
+    const int64_t tm = tm0 + lin % tiles_m;
+    lin /= tiles_m;
+    const int tn = static_cast<int>(lin % tiles_n);
+    const int ks = static_cast<int>(lin / tiles_n);
+    const int kb0 = ks * kb_per;
+    const int kb1 = min(nb, kb0 + kb_per);
+    const int n0 = tn * TN;
+    const int64_t row_bytes = static_cast<int64_t>(nb) * 18;
+
+    const int wk = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int lane = threadIdx.x & (kWave - 1);
+    const int li = lane & 15;
+    const int lg = lane >> 4;
+
+    uint32_t pre[LPT * 4];
+    auto fetch = [&](int c0) {
+        const int valid = min(KC, kb1 - c0) * 18;  // a multiple of 144
+#pragma unroll
+        for (int t = 0; t < LPT; ++t) {
+            const int p = t * kBlockThreads + static_cast<int>(threadIdx.x);
+            const int r = p / PR;
+            const int q = p - r * PR;
+            const int row = min(n0 + r, N - 1);             // rows past N: any valid row
+            const int off = (q * 16 < valid) ? q * 16 : 0;  // blocks past the split: any valid piece
+            const uint4 v = *reinterpret_cast<const uint4*>(W + row * row_bytes + static_cast<int64_t>(c0) * 18 + off);
+            pre[4 * t + 0] = v.x;
+            pre[4 * t + 1] = v.y;
+            pre[4 * t + 2] = v.z;
+            pre[4 * t + 3] = v.w;
+        }
+    };
+    auto stash = [&]() {
+#pragma unroll
+        for (int t = 0; t < LPT; ++t) {
+            const int p = t * kBlockThreads + static_cast<int>(threadIdx.x);
+            const int r = p / PR;
+            const int q = p - r * PR;
+            *reinterpret_cast<uint4*>(wt + r * (RS / 4) + q * 4) =
+                make_uint4(pre[4 * t], pre[4 * t + 1], pre[4 * t + 2], pre[4 * t + 3]);
+        }
+    };
+
+    float acc[MW][4];
+#pragma unroll
+    for (int mi = 0; mi < MW; ++mi)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[mi][r] = 0.0f;
+
+    struct AFrag {
+        h8 h[MW][2], l[MW][2];  // hi / lo of blocks b, b + 1
+        float s[MW][2][4];      // their scales, rows 4 lg .. 4 lg + 3
+    };
+
+    fetch(kb0);
+    for (int c0 = kb0; c0 < kb1; c0 += KC) {
+        __syncthreads();  // every wave is done with the previous chunk
+        stash();
+        __syncthreads();
+        if (c0 + KC < kb1) fetch(c0 + KC);
+        const int npair = min(KC, kb1 - c0) >> 1;
+        auto load_a = [&](int cp, AFrag& A) {
+            const int64_t b = c0 + 2 * cp;
+#pragma unroll
+            for (int mi = 0; mi < MW; ++mi) {
+                const int64_t mt = tm * MW + mi;
+#pragma unroll
+                for (int j = 0; j < 2; ++j) {
+                    const uint4* src = reinterpret_cast<const uint4*>(hl + ((mt * nb + b + j) * kWave + lane) * 32);
+                    A.h[mi][j] = __builtin_bit_cast(h8, src[0]);
+                    A.l[mi][j] = __builtin_bit_cast(h8, src[1]);
+                    const float4 sv = *reinterpret_cast<const float4*>(sx + (mt * nb + b + j) * 16 + 4 * lg);
+                    A.s[mi][j][0] = sv.x; A.s[mi][j][1] = sv.y; A.s[mi][j][2] = sv.z; A.s[mi][j][3] = sv.w;
+                }
+            }
+        };
+        auto mul_pair = [&](int cp, const AFrag& A) {
+            const uint32_t* rowp = wt + li * (RS / 4) + 9 * cp;
+            h8 bw[2];
+            float dw[2];
+            bw[0] = q4_codes_to_h8(__builtin_amdgcn_alignbyte(rowp[lg + 1], rowp[lg], 2));  // block b: codes 2 mod 4
+            bw[1] = q4_codes_to_h8(rowp[5 + lg]);                                         // block b + 1: aligned
+            dw[0] = half_bits_to_float(rowp[0] & 0xffffu);
+            dw[1] = half_bits_to_float(rowp[4] >> 16);
+#pragma unroll
+            for (int mi = 0; mi < MW; ++mi) {
+#pragma unroll
+                for (int j = 0; j < 2; ++j) {
+                    const v4f zero = {0.0f, 0.0f, 0.0f, 0.0f};
+                    v4f D = __builtin_amdgcn_mfma_f32_16x16x32_f16(A.h[mi][j], bw[j], zero, 0, 0, 0);
+                    D = __builtin_amdgcn_mfma_f32_16x16x32_f16(A.l[mi][j], bw[j], D, 0, 0, 0);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) acc[mi][r] = fmaf(D[r], dw[j] * A.s[mi][j][r], acc[mi][r]);
+                }
+            }
+        };
+        // the activations of the next pair are requested before the current
+        // pair is multiplied, with unconditional loads
+        if (wk < npair) {
+            AFrag A0, A1;
+            int cp = wk;
+            load_a(cp, A0);
+            while (true) {
+                load_a(min(cp + WK, npair - 1), A1);
+                mul_pair(cp, A0);
+                cp += WK;
+                if (cp >= npair) break;
+                load_a(min(cp + WK, npair - 1), A0);
+                mul_pair(cp, A1);
+                cp += WK;
+                if (cp >= npair) break;
+            }
+        }
+    }
+    __syncthreads();  // the weight tile is free
+    float* red = reinterpret_cast<float*>(wt);
+    if (wk > 0) {
+#pragma unroll
+        for (int v = 0; v < NV; ++v) red[((wk - 1) * NV + v) * kWave + lane] = acc[v / 4][v % 4];
+    }
+    __syncthreads();
+    if (wk == 0) {
+        for (int j = 1; j < WK; ++j) {
+#pragma unroll
+            for (int v = 0; v < NV; ++v) acc[v / 4][v % 4] += red[((j - 1) * NV + v) * kWave + lane];
+        }
+        float* o = out + (PARTIAL ? static_cast<int64_t>(ks) * M * N : 0);
+        const int n = n0 + li;
+#pragma unroll
+        for (int mi = 0; mi < MW; ++mi) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int64_t m = (tm * MW + mi) * 16 + 4 * lg + r;
+                if (m < M && n < N) o[m * N + n] = acc[mi][r];
+            }
+        }
+    }
+}
+
 // y = sum over K splits of the partial sums, in split order.
 __global__ __launch_bounds__(kBlockThreads)
 void qmm_reduce_kernel(const float* __restrict__ P, float* __restrict__ y, int ks, int64_t MN) {
@@ -787,6 +1060,62 @@ hipError_t launch_wide(const QmmPlan& p, const void* W, const int8_t* xa, const 
     return hipSuccess;
 }
 
+// Plan of qmm_q4_0_f32act for (N, K, M): M == 1 or K % 256 != 0 take the
+// float32 matrix-vector kernels row by row (no workspace); otherwise the
+// split activations, the float16 MFMA kernel (16 or 32 rows per tile) and,
+// when K is split across workgroups, the ordered reduction.
+struct F32ActPlan {
+    bool mfma = false;
+    int mw = 1;
+    int64_t tiles_m = 0;
+    int tiles_n = 0, ks = 1, kb = 0;
+    int64_t xrows = 0;
+    size_t hl_bytes = 0, s_bytes = 0, p_bytes = 0;
+};
+
+F32ActPlan plan_f32act(int64_t N, int64_t K, int64_t M) {
+    F32ActPlan p;
+    const int64_t nb = K / 32;
+    if (M == 1 || K % kUnitElems != 0) return p;
+    p.mfma = true;
+    p.mw = M > 16 ? 2 : 1;
+    p.tiles_m = ceil_div(M, 16 * p.mw);
+    p.tiles_n = static_cast<int>(ceil_div(N, 16));
+    const int64_t tiles = p.tiles_m * p.tiles_n;
+    // about 1024 workgroups, as for the narrow int8 tiling
+    int64_t ks = 1024 / tiles;
+    ks = ks < nb / 8 ? ks : nb / 8;
+    ks = ks > 1 ? ks : 1;
+    const int64_t kb = ceil_div(ceil_div(nb, ks), 8) * 8;
+    p.kb = static_cast<int>(kb);
+    p.ks = static_cast<int>(ceil_div(nb, kb));
+    p.xrows = p.tiles_m * 16 * p.mw;
+    p.hl_bytes = align256(static_cast<size_t>(p.xrows) * static_cast<size_t>(K) * 4);
+    p.s_bytes = align256(static_cast<size_t>(p.xrows) * static_cast<size_t>(nb) * sizeof(float));
+    p.p_bytes = p.ks > 1 ? align256(static_cast<size_t>(p.ks) * static_cast<size_t>(M) * static_cast<size_t>(N) *
+                                    sizeof(float))
+                         : 0;
+    return p;
+}
+
+template <int MW, bool PARTIAL>
+hipError_t launch_f16(const F32ActPlan& p, const void* W, const uint8_t* hl, const float* sx, float* out, int64_t N,
+                      int64_t K, int64_t M, hipStream_t stream) {
+    const int64_t per_mt = static_cast<int64_t>(p.tiles_n) * p.ks;
+    int64_t mt_slice = (int64_t{1} << 30) / per_mt;
+    mt_slice = mt_slice < p.tiles_m ? mt_slice : p.tiles_m;
+    for (int64_t tm0 = 0; tm0 < p.tiles_m; tm0 += mt_slice) {
+        const int64_t tms = (p.tiles_m - tm0 < mt_slice) ? p.tiles_m - tm0 : mt_slice;
+        const int64_t nwg = tms * per_mt;
+        hipLaunchKernelGGL((qmm_f16_kernel<MW, 128, PARTIAL>), dim3(static_cast<unsigned>(nwg)), dim3(kBlockThreads),
+                           0, stream, static_cast<const uint8_t*>(W), hl, sx, out, static_cast<int>(N), M,
+                           static_cast<int>(K / 32), tm0, tms, p.tiles_n, p.kb, nwg);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
 // The M == 1 and K % 256 != 0 paths (row-major activation codes).
 hipError_t launch_dot(const QmmPlan& p, const void* W, const int8_t* qx, const float* dx, float* y, int32_t* isum,
                       int64_t N64, int64_t K, int64_t M, hipStream_t stream) {
@@ -871,6 +1200,54 @@ hipError_t launch_q4_0_q8_blocksums(const void* W, const int8_t* qx, int32_t* is
     if (p.path == kPathNarrow)
         return launch_mfma<QMM_NARROW, kModeISum>(p, W, qx, nullptr, nullptr, isum, N, K, M, stream);
     return launch_dot(p, W, qx, nullptr, nullptr, isum, N, K, M, stream);
+}
+
+size_t qmm_f32act_ws_bytes(int64_t N, int64_t K, int64_t M) {
+    const F32ActPlan p = plan_f32act(N, K, M);
+    const size_t b = p.hl_bytes + p.s_bytes + p.p_bytes;
+    return b > 256 ? b : 256;
+}
+
+hipError_t launch_qmm_f32act(const void* W, const float* x, float* y, int64_t N, int64_t K, int64_t M, void* ws,
+                             hipStream_t stream) {
+    const F32ActPlan p = plan_f32act(N, K, M);
+    if (!p.mfma) {
+        for (int64_t m = 0; m < M; ++m) {
+            const hipError_t e = launch_gemv(0, W, nullptr, x + m * K, y + m * N, N, K, stream);
+            if (e != hipSuccess) return e;
+        }
+        return hipSuccess;
+    }
+    uint8_t* hl = static_cast<uint8_t*>(ws);
+    float* sx = reinterpret_cast<float*>(static_cast<char*>(ws) + p.hl_bytes);
+    float* part = reinterpret_cast<float*>(static_cast<char*>(ws) + p.hl_bytes + p.s_bytes);
+    {
+        const int64_t groups = p.xrows * (K / 32);
+        int64_t blocks = ceil_div(groups * 8, kBlockThreads);
+        const int64_t cap = static_cast<int64_t>(device_cus()) * 64;
+        if (blocks > cap) blocks = cap;
+        const bool vec_x = (reinterpret_cast<uintptr_t>(x) & 15) == 0;
+        hipLaunchKernelGGL(split_f16_kernel, dim3(static_cast<unsigned>(blocks)), dim3(kBlockThreads), 0, stream, x,
+                           hl, sx, K, M, p.xrows, vec_x);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    hipError_t e;
+    if (p.ks == 1) {
+        e = p.mw == 2 ? launch_f16<2, false>(p, W, hl, sx, y, N, K, M, stream)
+                      : launch_f16<1, false>(p, W, hl, sx, y, N, K, M, stream);
+        return e;
+    }
+    e = p.mw == 2 ? launch_f16<2, true>(p, W, hl, sx, part, N, K, M, stream)
+                  : launch_f16<1, true>(p, W, hl, sx, part, N, K, M, stream);
+    if (e != hipSuccess) return e;
+    const int64_t MN = M * N;
+    int64_t blocks = ceil_div(MN, kBlockThreads);
+    const int64_t cap = static_cast<int64_t>(device_cus()) * 8;
+    if (blocks > cap) blocks = cap;
+    hipLaunchKernelGGL(qmm_reduce_kernel, dim3(static_cast<unsigned>(blocks)), dim3(kBlockThreads), 0, stream, part,
+                       y, p.ks, MN);
+    return hipGetLastError();
 }
 
 }  // namespace qmv

@@ -105,6 +105,21 @@ int qmm_q4_0_q8act(const void* W, const float* x, float* y, int64_t N, int64_t K
     return launched(qmv::launch_qmm_q8act(W, x, y, N, K, M, ws, stream));
 }
 
+size_t qmm_q4_0_f32act_ws_bytes(int64_t N, int64_t K, int64_t M) {
+    if (check_shape(N, K, M, 32, 18) != QMV_OK) return 0;
+    return qmv::qmm_f32act_ws_bytes(N, K, M);
+}
+
+int qmm_q4_0_f32act(const void* W, const float* x, float* y, int64_t N, int64_t K, int64_t M, void* ws,
+                    size_t ws_bytes, hipStream_t stream) {
+    if (!W || !x || !y || !ws) return QMV_ERR_NULL;
+    int rc = check_shape(N, K, M, 32, 18);
+    if (rc) return rc;
+    if (!aligned(W, 16) || !aligned(x, 4) || !aligned(y, 4) || !aligned(ws, 16)) return QMV_ERR_ALIGN;
+    if (ws_bytes < qmm_q4_0_f32act_ws_bytes(N, K, M)) return QMV_ERR_WORKSPACE;
+    return launched(qmv::launch_qmm_f32act(W, x, y, N, K, M, ws, stream));
+}
+
 size_t logits_topk_ws_bytes(int64_t N, int64_t M, int32_t k) {
     if (N < 1 || M < 1 || k < 1 || N > kMaxN) return 0;
     int64_t t;

@@ -37,4 +37,10 @@ hipError_t launch_qmm_q8act(const void* W, const float* x, float* y, int64_t N, 
 hipError_t launch_q4_0_q8_blocksums(const void* W, const int8_t* qx, int32_t* isum, int64_t N,
                                     int64_t K, int64_t M, hipStream_t stream);
 
+// Q4_0 x float32 activations (small M).  The workspace layout (and size)
+// depends on (N, K, M) only.
+size_t qmm_f32act_ws_bytes(int64_t N, int64_t K, int64_t M);
+hipError_t launch_qmm_f32act(const void* W, const float* x, float* y, int64_t N, int64_t K, int64_t M,
+                             void* ws, hipStream_t stream);
+
 }  // namespace qmv

@@ -33,6 +33,8 @@ _SIGS = {
     "qmv_q4_0_geglu": ([_P, _P, _P, _P, _I64, _I64, _I64, _P], ctypes.c_int),
     "qmm_q4_0_q8act_ws_bytes": ([_I64, _I64, _I64], _SZ),
     "qmm_q4_0_q8act": ([_P, _P, _P, _I64, _I64, _I64, _P, _SZ, _P], ctypes.c_int),
+    "qmm_q4_0_f32act_ws_bytes": ([_I64, _I64, _I64], _SZ),
+    "qmm_q4_0_f32act": ([_P, _P, _P, _I64, _I64, _I64, _P, _SZ, _P], ctypes.c_int),
     "logits_topk_ws_bytes": ([_I64, _I64, _I32], _SZ),
     "logits_topk": ([_P, _P, _P, _P, _I64, _I64, _I64, _I32, _F, _P, _SZ, _P], ctypes.c_int),
     "qmvdbg_quantize_q8": ([_P, _P, _P, _I64, _I64, _P], ctypes.c_int),
@@ -103,6 +105,14 @@ def qmm_q4_0_q8act_ws_bytes(N, K, M) -> int:
 
 def qmm_q4_0_q8act(W, x, y, N, K, M, ws, ws_bytes, stream=None):
     _call("qmm_q4_0_q8act", _ptr(W), _ptr(x), _ptr(y), N, K, M, _ptr(ws), ws_bytes, _stream(stream))
+
+
+def qmm_q4_0_f32act_ws_bytes(N, K, M) -> int:
+    return int(lib.qmm_q4_0_f32act_ws_bytes(N, K, M))
+
+
+def qmm_q4_0_f32act(W, x, y, N, K, M, ws, ws_bytes, stream=None):
+    _call("qmm_q4_0_f32act", _ptr(W), _ptr(x), _ptr(y), N, K, M, _ptr(ws), ws_bytes, _stream(stream))
 
 
 def logits_topk_ws_bytes(N, M, k) -> int:

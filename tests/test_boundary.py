@@ -26,7 +26,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported_and_bound():
     names = declared_functions()
-    assert "qmv_q4_0" in names and "logits_topk" in names and len(names) == 12
+    assert "qmv_q4_0" in names and "logits_topk" in names and len(names) == 14
     for n in names:
         assert hasattr(qmv.lib, n), n
     assert sorted(qmv.EXPORTS) == names
@@ -100,6 +100,23 @@ def test_qmm_validation_and_workspace():
     assert call("qmm_q4_0_q8act", FAKE, FAKE, FAKE, 8, 64, 1, FAKE + 4, 1 << 20, S) == ALIGN
     assert call("qmm_q4_0_q8act", FAKE, FAKE, FAKE, 8, 40, 1, FAKE, 1 << 20, S) == SHAPE
     assert call("qmm_q4_0_q8act", None, FAKE, FAKE, 8, 64, 1, FAKE, 1 << 20, S) == NUL
+
+
+def test_qmm_f32act_validation_and_workspace():
+    # split activations: two float16 terms per element (4 B) plus a scale per block
+    need = qmv.qmm_q4_0_f32act_ws_bytes(21504, 5376, 8)
+    assert need >= 16 * 5376 * 4 + 16 * 168 * 4
+    assert qmv.qmm_q4_0_f32act_ws_bytes(21504, 5376, 32) >= 32 * 5376 * 4 + 32 * 168 * 4
+    # M == 1 and K % 256 != 0 use the matrix-vector kernels: a token workspace
+    assert qmv.qmm_q4_0_f32act_ws_bytes(8, 96, 3) == 256
+    assert qmv.qmm_q4_0_f32act_ws_bytes(8, 33, 2) == 0
+    assert qmv.qmm_q4_0_f32act_ws_bytes(8, 256, 0) == 0
+    assert call("qmm_q4_0_f32act", FAKE, FAKE, FAKE, 8, 256, 2, None, 1 << 20, S) == NUL
+    assert call("qmm_q4_0_f32act", FAKE, FAKE, FAKE, 8, 256, 2, FAKE, 16, S) == WS
+    assert call("qmm_q4_0_f32act", FAKE, FAKE, FAKE, 8, 256, 2, FAKE + 4, 1 << 20, S) == ALIGN
+    assert call("qmm_q4_0_f32act", FAKE + 8, FAKE, FAKE, 8, 256, 2, FAKE, 1 << 20, S) == ALIGN
+    assert call("qmm_q4_0_f32act", FAKE, FAKE, FAKE, 8, 40, 2, FAKE, 1 << 20, S) == SHAPE
+    assert call("qmm_q4_0_f32act", FAKE, FAKE, None, 8, 256, 2, FAKE, 1 << 20, S) == NUL
 
 
 def test_logits_topk_validation():

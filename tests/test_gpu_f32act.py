@@ -1,0 +1,91 @@
+"""Parity of qmm_q4_0_f32act (Q4_0 weights x float32 activations, a few rows
+at once) with the float64 oracle of the matrix-vector product, element by
+element, through the C ABI.  Bar: |y - y_ref| <= 1e-5 * sum_i |w_i x_i| + 1e-6,
+the float32 bar of qmv_q4_0: the activations are not quantized."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from quantized_dequant_matrix_amd import synth
+from gpu_util import assert_within, dev, empty, host, say
+
+pytestmark = pytest.mark.gpu
+
+C2 = synth.CONFIGS["c2"]
+
+
+def gpu_f32act(W, x, N, K, M):
+    from quantized_dequant_matrix_amd import qmv
+    wsb = qmv.qmm_q4_0_f32act_ws_bytes(N, K, M)
+    ws = torch.empty(wsb, dtype=torch.uint8, device="cuda:0")
+    y = empty((M, N))
+    qmv.qmm_q4_0_f32act(dev(W), dev(x), y, N, K, M, ws, wsb)
+    return host(y)
+
+
+# one and two 16-row tiles per workgroup tile, ragged M and N, K split across
+# workgroups or not, and the row-by-row paths (M == 1, K % 256 != 0)
+@pytest.mark.parametrize("N,K,M", [(16, 256, 2), (65, 512, 8), (129, 5376, 8), (200, 5376, 17), (31, 2048, 32),
+                                   (300, 21504, 33), (1000, 256, 16), (5, 96, 3), (70, 256, 1), (3, 4096, 5)])
+def test_shapes(N, K, M):
+    seed = 11 * N + K + M
+    say(f"qmm_q4_0_f32act N={N} K={K} M={M} seed={seed}")
+    W, x = synth.problem("q4_0", N, K, M, seed)
+    y = gpu_f32act(W, x, N, K, M)
+    yr, S = oracle.qmv("q4_0", W, N, K, x, M=M)
+    assert_within(y, yr, oracle.float_tol(S), f"f32act {N}x{K} M={M}")
+
+
+def test_verifier_batch_at_the_ffn_shape():
+    """The fixed-eight verifier batch on the 21504 x 5376 Q4_0 matrix, every output."""
+    N, K, M = C2["N"], C2["K"], 8
+    say(f"qmm_q4_0_f32act N={N} K={K} M={M}")
+    W, _ = synth.config_problem("c2")
+    x = synth.activations(M, K, 2102)
+    y = gpu_f32act(W, x, N, K, M)
+    yr, S = oracle.qmv("q4_0", W, N, K, x, M=M)
+    w = assert_within(y, yr, oracle.float_tol(S), "verifier M=8")
+    say(f"verifier M=8: worst err/tol {w:.3g}")
+
+
+def test_prefill_tile_at_the_ffn_shape_sampled():
+    N, K, M = C2["N"], C2["K"], 32
+    say(f"qmm_q4_0_f32act N={N} K={K} M={M}, sampled rows")
+    W, _ = synth.config_problem("c2")
+    x = synth.activations(M, K, 2132)
+    y = gpu_f32act(W, x, N, K, M)
+    rows = np.sort(np.random.default_rng(6).choice(N, 64, replace=False))
+    yr, S = oracle.qmv("q4_0", W, N, K, x, M=M, rows=rows)
+    assert_within(y[:, rows], yr, oracle.float_tol(S), "prefill M=32")
+    assert np.all(np.isfinite(y))
+
+
+def test_wide_dynamic_range():
+    """Blocks scaled from 1e-30 to 1e30, an all-zero block, and tiny elements
+    beside large ones inside a block: the per-block power-of-two scale keeps
+    the float16 split within the float32 bar."""
+    N, K, M = 96, 2048, 6
+    W, x = synth.problem("q4_0", N, K, M, 4242)
+    rng = np.random.default_rng(3)
+    blocks = x.reshape(M, K // 32, 32)
+    blocks *= (10.0 ** rng.uniform(-30, 30, size=(M, K // 32, 1))).astype(np.float32)
+    blocks[1, 5] = 0.0
+    blocks[2, 7, :16] *= np.float32(1e-12)
+    x = blocks.reshape(M, K).astype(np.float32)
+    say("qmm_q4_0_f32act wide dynamic range")
+    y = gpu_f32act(W, x, N, K, M)
+    yr, S = oracle.qmv("q4_0", W, N, K, x, M=M)
+    assert_within(y, yr, oracle.float_tol(S), "f32act dynamic range")
+
+
+def test_agrees_with_the_matrix_vector_path():
+    from quantized_dequant_matrix_amd import qmv
+    N, K, M = 513, 5376, 12
+    W, x = synth.problem("q4_0", N, K, M, 515)
+    say("qmm_q4_0_f32act vs qmv_q4_0 row by row")
+    y = gpu_f32act(W, x, N, K, M)
+    y1 = empty((M, N))
+    qmv.qmv_q4_0(dev(W), dev(x), y1, N, K, M)
+    _, S = oracle.qmv("q4_0", W, N, K, x, M=M)
+    assert_within(y, host(y1), 2 * oracle.float_tol(S), "f32act vs qmv")
