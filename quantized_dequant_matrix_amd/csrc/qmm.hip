@@ -772,24 +772,27 @@ __device__ __forceinline__ h8 q4_codes_to_h8(uint32_t c) {
     return h8{a[0], a[1], b[0], b[1], c2[0], c2[1], d[0], d[1]};
 }
 
-// 16 MW rows of m x 16 weight rows per workgroup; the four waves split each
-// chunk's block pairs, their sums are added in LDS in wave order, and K may
-// be split across workgroups (PARTIAL: write split ks of the partial sums).
-// The weight chunk is staged as raw GGUF bytes (16 rows x KC blocks) with
-// 16-byte loads, the next chunk prefetched into registers.
-template <int MW, int KC, bool PARTIAL>
+// 16 MW rows of m x 16 NW weight rows per workgroup: every wave multiplies
+// all of them, the four waves split each chunk's block pairs, their sums are
+// added in LDS in wave order, and K may be split across workgroups
+// (PARTIAL: write split ks of the partial sums).  The weight chunk is staged
+// as raw GGUF bytes (16 NW rows x KC blocks) with 16-byte loads, the next
+// chunk prefetched into registers.  The activation loads are the costly
+// traffic here (32 bytes per lane per block and m-tile from the caches), so
+// each is used for NW weight tiles.
+template <int MW, int NW, int KC, bool PARTIAL>
 __global__ __launch_bounds__(kBlockThreads)
 void qmm_f16_kernel(const uint8_t* __restrict__ W, const uint8_t* __restrict__ hl, const float* __restrict__ sx,
                     float* __restrict__ out, int N, int64_t M, int nb, int64_t tm0, int64_t tiles_m, int tiles_n,
                     int kb_per, int64_t nwg) {
-    constexpr int TN = 16;
+    constexpr int TN = 16 * NW;
     constexpr int WK = kWavesPerBlock;
     constexpr int RB = KC * 18;
     constexpr int RS = RB + 16;  // LDS row stride: rows 4 banks apart (mod 64)
     constexpr int PR = RB / 16;
     constexpr int LPT = TN * PR / kBlockThreads;
     static_assert(KC % 8 == 0 && TN * PR == LPT * kBlockThreads, "the weight chunk must split evenly");
-    constexpr int NV = MW * 4;
+    constexpr int NV = MW * NW * 4;
     static_assert((WK - 1) * NV * kWave <= TN * RS / 4, "the reduction fits the weight tile");
     __shared__ __align__(16) uint32_t wt[TN * RS / 4];
 
@@ -837,11 +840,13 @@ void qmm_f16_kernel(const uint8_t* __restrict__ W, const uint8_t* __restrict__ h
         }
     };
 
-    float acc[MW][4];
+    float acc[MW][NW][4];
 #pragma unroll
     for (int mi = 0; mi < MW; ++mi)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) acc[mi][r] = 0.0f;
+        for (int ni = 0; ni < NW; ++ni)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) acc[mi][ni][r] = 0.0f;
 
     struct AFrag {
         h8 h[MW][2], l[MW][2];  // hi / lo of blocks b, b + 1
@@ -855,38 +860,51 @@ void qmm_f16_kernel(const uint8_t* __restrict__ W, const uint8_t* __restrict__ h
         __syncthreads();
         if (c0 + KC < kb1) fetch(c0 + KC);
         const int npair = min(KC, kb1 - c0) >> 1;
+        // Rows past M are zero in the split layout; their lanes skip the loads.
         auto load_a = [&](int cp, AFrag& A) {
             const int64_t b = c0 + 2 * cp;
 #pragma unroll
             for (int mi = 0; mi < MW; ++mi) {
                 const int64_t mt = tm * MW + mi;
+                const bool arow = mt * 16 + li < M;        // A operand row of this lane
+                const bool orow = mt * 16 + 4 * lg < M;    // first output row of this lane
 #pragma unroll
                 for (int j = 0; j < 2; ++j) {
-                    const uint4* src = reinterpret_cast<const uint4*>(hl + ((mt * nb + b + j) * kWave + lane) * 32);
-                    A.h[mi][j] = __builtin_bit_cast(h8, src[0]);
-                    A.l[mi][j] = __builtin_bit_cast(h8, src[1]);
-                    const float4 sv = *reinterpret_cast<const float4*>(sx + (mt * nb + b + j) * 16 + 4 * lg);
+                    h8 hv = {}, lv = {};
+                    if (arow) {
+                        const uint4* src = reinterpret_cast<const uint4*>(hl + ((mt * nb + b + j) * kWave + lane) * 32);
+                        hv = __builtin_bit_cast(h8, src[0]);
+                        lv = __builtin_bit_cast(h8, src[1]);
+                    }
+                    A.h[mi][j] = hv;
+                    A.l[mi][j] = lv;
+                    float4 sv = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+                    if (orow) sv = *reinterpret_cast<const float4*>(sx + (mt * nb + b + j) * 16 + 4 * lg);
                     A.s[mi][j][0] = sv.x; A.s[mi][j][1] = sv.y; A.s[mi][j][2] = sv.z; A.s[mi][j][3] = sv.w;
                 }
             }
         };
         auto mul_pair = [&](int cp, const AFrag& A) {
-            const uint32_t* rowp = wt + li * (RS / 4) + 9 * cp;
-            h8 bw[2];
-            float dw[2];
-            bw[0] = q4_codes_to_h8(__builtin_amdgcn_alignbyte(rowp[lg + 1], rowp[lg], 2));  // block b: codes 2 mod 4
-            bw[1] = q4_codes_to_h8(rowp[5 + lg]);                                         // block b + 1: aligned
-            dw[0] = half_bits_to_float(rowp[0] & 0xffffu);
-            dw[1] = half_bits_to_float(rowp[4] >> 16);
 #pragma unroll
-            for (int mi = 0; mi < MW; ++mi) {
+            for (int ni = 0; ni < NW; ++ni) {
+                const uint32_t* rowp = wt + (ni * 16 + li) * (RS / 4) + 9 * cp;
+                h8 bw[2];
+                float dw[2];
+                bw[0] = q4_codes_to_h8(__builtin_amdgcn_alignbyte(rowp[lg + 1], rowp[lg], 2));  // block b: codes 2 mod 4
+                bw[1] = q4_codes_to_h8(rowp[5 + lg]);                                         // block b + 1: aligned
+                dw[0] = half_bits_to_float(rowp[0] & 0xffffu);
+                dw[1] = half_bits_to_float(rowp[4] >> 16);
 #pragma unroll
-                for (int j = 0; j < 2; ++j) {
-                    const v4f zero = {0.0f, 0.0f, 0.0f, 0.0f};
-                    v4f D = __builtin_amdgcn_mfma_f32_16x16x32_f16(A.h[mi][j], bw[j], zero, 0, 0, 0);
-                    D = __builtin_amdgcn_mfma_f32_16x16x32_f16(A.l[mi][j], bw[j], D, 0, 0, 0);
+                for (int mi = 0; mi < MW; ++mi) {
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) acc[mi][r] = fmaf(D[r], dw[j] * A.s[mi][j][r], acc[mi][r]);
+                    for (int j = 0; j < 2; ++j) {
+                        const v4f zero = {0.0f, 0.0f, 0.0f, 0.0f};
+                        v4f D = __builtin_amdgcn_mfma_f32_16x16x32_f16(A.h[mi][j], bw[j], zero, 0, 0, 0);
+                        D = __builtin_amdgcn_mfma_f32_16x16x32_f16(A.l[mi][j], bw[j], D, 0, 0, 0);
+#pragma unroll
+                        for (int r = 0; r < 4; ++r)
+                            acc[mi][ni][r] = fmaf(D[r], dw[j] * A.s[mi][j][r], acc[mi][ni][r]);
+                    }
                 }
             }
         };
@@ -912,22 +930,25 @@ void qmm_f16_kernel(const uint8_t* __restrict__ W, const uint8_t* __restrict__ h
     float* red = reinterpret_cast<float*>(wt);
     if (wk > 0) {
 #pragma unroll
-        for (int v = 0; v < NV; ++v) red[((wk - 1) * NV + v) * kWave + lane] = acc[v / 4][v % 4];
+        for (int v = 0; v < NV; ++v) red[((wk - 1) * NV + v) * kWave + lane] = acc[v / (NW * 4)][(v / 4) % NW][v % 4];
     }
     __syncthreads();
     if (wk == 0) {
         for (int j = 1; j < WK; ++j) {
 #pragma unroll
-            for (int v = 0; v < NV; ++v) acc[v / 4][v % 4] += red[((j - 1) * NV + v) * kWave + lane];
+            for (int v = 0; v < NV; ++v) acc[v / (NW * 4)][(v / 4) % NW][v % 4] += red[((j - 1) * NV + v) * kWave + lane];
         }
         float* o = out + (PARTIAL ? static_cast<int64_t>(ks) * M * N : 0);
-        const int n = n0 + li;
 #pragma unroll
-        for (int mi = 0; mi < MW; ++mi) {
+        for (int ni = 0; ni < NW; ++ni) {
+            const int n = n0 + ni * 16 + li;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int64_t m = (tm * MW + mi) * 16 + 4 * lg + r;
-                if (m < M && n < N) o[m * N + n] = acc[mi][r];
+            for (int mi = 0; mi < MW; ++mi) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int64_t m = (tm * MW + mi) * 16 + 4 * lg + r;
+                    if (m < M && n < N) o[m * N + n] = acc[mi][ni][r];
+                }
             }
         }
     }
@@ -1066,7 +1087,7 @@ hipError_t launch_wide(const QmmPlan& p, const void* W, const int8_t* xa, const 
 // when K is split across workgroups, the ordered reduction.
 struct F32ActPlan {
     bool mfma = false;
-    int mw = 1;
+    int mw = 1, nw = 2;  // 16-row tiles of m per workgroup, of n per wave
     int64_t tiles_m = 0;
     int tiles_n = 0, ks = 1, kb = 0;
     int64_t xrows = 0;
@@ -1078,9 +1099,12 @@ F32ActPlan plan_f32act(int64_t N, int64_t K, int64_t M) {
     const int64_t nb = K / 32;
     if (M == 1 || K % kUnitElems != 0) return p;
     p.mfma = true;
+    // one 16-row m-tile with two n-tiles per wave, or two m-tiles with four:
+    // more n-tiles per wave share each activation load
     p.mw = M > 16 ? 2 : 1;
+    p.nw = M > 16 ? 4 : 2;
     p.tiles_m = ceil_div(M, 16 * p.mw);
-    p.tiles_n = static_cast<int>(ceil_div(N, 16));
+    p.tiles_n = static_cast<int>(ceil_div(N, 16 * p.nw));
     const int64_t tiles = p.tiles_m * p.tiles_n;
     // about 1024 workgroups, as for the narrow int8 tiling
     int64_t ks = 1024 / tiles;
@@ -1098,7 +1122,7 @@ F32ActPlan plan_f32act(int64_t N, int64_t K, int64_t M) {
     return p;
 }
 
-template <int MW, bool PARTIAL>
+template <int MW, int NW, int KC, bool PARTIAL>
 hipError_t launch_f16(const F32ActPlan& p, const void* W, const uint8_t* hl, const float* sx, float* out, int64_t N,
                       int64_t K, int64_t M, hipStream_t stream) {
     const int64_t per_mt = static_cast<int64_t>(p.tiles_n) * p.ks;
@@ -1107,7 +1131,7 @@ hipError_t launch_f16(const F32ActPlan& p, const void* W, const uint8_t* hl, con
     for (int64_t tm0 = 0; tm0 < p.tiles_m; tm0 += mt_slice) {
         const int64_t tms = (p.tiles_m - tm0 < mt_slice) ? p.tiles_m - tm0 : mt_slice;
         const int64_t nwg = tms * per_mt;
-        hipLaunchKernelGGL((qmm_f16_kernel<MW, 128, PARTIAL>), dim3(static_cast<unsigned>(nwg)), dim3(kBlockThreads),
+        hipLaunchKernelGGL((qmm_f16_kernel<MW, NW, KC, PARTIAL>), dim3(static_cast<unsigned>(nwg)), dim3(kBlockThreads),
                            0, stream, static_cast<const uint8_t*>(W), hl, sx, out, static_cast<int>(N), M,
                            static_cast<int>(K / 32), tm0, tms, p.tiles_n, p.kb, nwg);
         const hipError_t e = hipGetLastError();
@@ -1233,13 +1257,14 @@ hipError_t launch_qmm_f32act(const void* W, const float* x, float* y, int64_t N,
         if (e != hipSuccess) return e;
     }
     hipError_t e;
+    // weight chunks: 32 rows x 64 blocks or 64 rows x 32 blocks (37 KB of LDS)
     if (p.ks == 1) {
-        e = p.mw == 2 ? launch_f16<2, false>(p, W, hl, sx, y, N, K, M, stream)
-                      : launch_f16<1, false>(p, W, hl, sx, y, N, K, M, stream);
+        e = p.mw == 2 ? launch_f16<2, 4, 32, false>(p, W, hl, sx, y, N, K, M, stream)
+                      : launch_f16<1, 2, 64, false>(p, W, hl, sx, y, N, K, M, stream);
         return e;
     }
-    e = p.mw == 2 ? launch_f16<2, true>(p, W, hl, sx, part, N, K, M, stream)
-                  : launch_f16<1, true>(p, W, hl, sx, part, N, K, M, stream);
+    e = p.mw == 2 ? launch_f16<2, 4, 32, true>(p, W, hl, sx, part, N, K, M, stream)
+                  : launch_f16<1, 2, 64, true>(p, W, hl, sx, part, N, K, M, stream);
     if (e != hipSuccess) return e;
     const int64_t MN = M * N;
     int64_t blocks = ceil_div(MN, kBlockThreads);
