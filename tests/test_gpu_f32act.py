@@ -89,3 +89,19 @@ def test_agrees_with_the_matrix_vector_path():
     qmv.qmv_q4_0(dev(W), dev(x), y1, N, K, M)
     _, S = oracle.qmv("q4_0", W, N, K, x, M=M)
     assert_within(y, host(y1), 2 * oracle.float_tol(S), "f32act vs qmv")
+
+
+def test_unaligned_activations():
+    """x only 4-byte aligned: the split kernel reads it element by element."""
+    from quantized_dequant_matrix_amd import qmv
+    N, K, M = 70, 1024, 9
+    W, x = synth.problem("q4_0", N, K, M, 909)
+    say("qmm_q4_0_f32act with x at a 4-byte offset")
+    buf = torch.zeros(M * K + 1, dtype=torch.float32, device="cuda:0")
+    buf[1:] = dev(x).reshape(-1)
+    wsb = qmv.qmm_q4_0_f32act_ws_bytes(N, K, M)
+    ws = torch.empty(wsb, dtype=torch.uint8, device="cuda:0")
+    y = empty((M, N))
+    qmv.qmm_q4_0_f32act(dev(W), buf.data_ptr() + 4, y, N, K, M, ws, wsb)
+    yr, S = oracle.qmv("q4_0", W, N, K, x, M=M)
+    assert_within(host(y), yr, oracle.float_tol(S), "f32act unaligned x")
