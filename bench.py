@@ -320,11 +320,35 @@ def measure_rows(torch, qmv, synth, dev):
     y = torch.empty((1, c["N"]), device=dev)
     ms = _time_loop(torch, lambda i: qmv.qmv_q8_0(Wd, xd, y, c["N"], c["K"], 1), 20, warm=3)
     res["c3_qmv_q8_0_only_262144x5376"] = {"us": ms * 1e3, "bytes": b, "GB/s": b / ms / 1e6}
+    # token selection on the device: top-40, then a top-p draw (0.95, T = 1)
+    k40 = 40
+    wsb40 = qmv.logits_topk_ws_bytes(c["N"], 1, k40)
+    ws40 = torch.empty(wsb40, dtype=torch.uint8, device=dev)
+    v40 = torch.empty((1, k40), device=dev)
+    i40 = torch.empty((1, k40), dtype=torch.int32, device=dev)
+    ud = torch.full((1,), 0.5, device=dev)
+    tok = torch.empty((1,), dtype=torch.int32, device=dev)
+    nuc = torch.empty((1,), dtype=torch.int32, device=dev)
+    ms = _time_loop(torch, lambda i: qmv.logits_sample(Wd, xd, ud, tok, nuc, v40, i40, c["N"], c["K"], 1, k40,
+                                                       c["softcap"], 1.0, 0.95, ws40, wsb40), 20, warm=3)
+    res["c3_logits_sample_q8_0_262144x5376_k40_p0.95"] = {"us": ms * 1e3, "bytes": b, "GB/s": b / ms / 1e6}
     # the two-stage top-k alone, on the same logits
     yl = ylog.clone().reshape(1, -1)
     ms = _time_loop(torch, lambda i: qmv.qmvdbg_topk_f32(yl, vals, idx, c["N"], 1, k, c["softcap"], ws, wsb), 50,
                     warm=3)
     res["c3_topk_only_262144_k10"] = {"us": ms * 1e3, "bytes": c["N"] * 4, "GB/s": c["N"] * 4 / ms / 1e6}
+    del Wd
+    # the 1024-wide drafter projection over the same vocabulary (Q8_0 262144 x 1024) + selection
+    Kd = 1024
+    Wm = t(synth.q8_0_weights(c["N"], Kd, 1103))
+    xm = t(synth.activations(1, Kd, 1104))
+    ms = _time_loop(torch, lambda i: qmv.logits_sample(Wm, xm, ud, tok, nuc, v40, i40, c["N"], Kd, 1, k40,
+                                                       c["softcap"], 1.0, 0.95, ws40, wsb40), 50, warm=3)
+    bm = Wm.numel() + Kd * 4 + c["N"] * 4
+    res["mtp_logits_sample_q8_0_262144x1024_k40_p0.95"] = {"us": ms * 1e3, "bytes": bm, "GB/s": bm / ms / 1e6}
+    ms = _time_loop(torch, lambda i: qmv.qmv_q8_0(Wm, xm, y, c["N"], Kd, 1), 50, warm=3)
+    res["mtp_qmv_q8_0_only_262144x1024"] = {"us": ms * 1e3, "bytes": bm, "GB/s": bm / ms / 1e6}
+    del Wm
     # a plain device-to-device copy of 256 MB (read + write), next to the GEMV rates
     a = torch.empty(256 * 1000 * 1000, dtype=torch.uint8, device=dev).fill_(1)
     bb = torch.empty_like(a)

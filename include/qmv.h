@@ -165,6 +165,24 @@ int logits_topk(const void* W_q8_0, const float* x, float* top_val, int32_t* top
                 int64_t N, int64_t K, int64_t M, int32_t k, float softcap,
                 void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* Token selection on the device after the logit projection: logits_topk,
+ * then one draw per row from the k selected pairs.
+ *   w_i = exp((top_val[m][i] - top_val[m][0]) / temperature), i < k
+ *         (NaN values weigh 0);
+ *   nucleus[m] = the smallest n >= 1 with w_0 + ... + w_{n-1} >= top_p * (w_0 + ... + w_{k-1});
+ *   token[m] = top_idx[m][j] for the first j < n with
+ *         w_0 + ... + w_j > u[m] * (w_0 + ... + w_{n-1})   (j = n - 1 if none);
+ * all in float32, the prefix sums in one fixed order, so the draw is a
+ * deterministic function of u.  u: device float32 [M], each in [0, 1), from
+ * the caller's generator.  temperature > 0 and finite, 0 < top_p <= 1.
+ * top_val / top_idx receive the k pairs as in logits_topk.
+ * [roadmap K5: top-k40 / top-p tokens selected on the device after the tied
+ *  output projection, with a (value, token) frontier]
+ * ws: as logits_topk (logits_topk_ws_bytes(N, M, k) bytes). */
+int logits_sample(const void* W_q8_0, const float* x, const float* u, int32_t* token, int32_t* nucleus,
+                  float* top_val, int32_t* top_idx, int64_t N, int64_t K, int64_t M, int32_t k, float softcap,
+                  float temperature, float top_p, void* ws, size_t ws_bytes, hipStream_t stream);
+
 /* ---- diagnostics: expose intermediate results of the paths above so
  * that tests can check them bit for bit ---- */
 
@@ -182,6 +200,12 @@ int qmvdbg_q4_0_q8_blocksums(const void* W, const int8_t* qx, int32_t* isum,
 int qmvdbg_topk_f32(const float* y, float* top_val, int32_t* top_idx,
                     int64_t N, int64_t M, int32_t k, float softcap,
                     void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* The draw of logits_sample alone, on given sorted pairs top_val / top_idx
+ * [M][k] (k <= 64). */
+int qmvdbg_sample_f32(const float* top_val, const int32_t* top_idx, const float* u,
+                      int32_t* token, int32_t* nucleus, int64_t M, int32_t k,
+                      float temperature, float top_p, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -62,6 +62,8 @@ def _load():
     lib.oracle_q4_0_q8_blocksums.argtypes = [P, I64, I64, P, I64, P, I64, P]
     lib.oracle_qmm_q4_0_q8.argtypes = [P, I64, I64, P, P, I64, P, I64, P, P]
     lib.oracle_topk.argtypes = [P, I64, ctypes.c_int32, P]
+    lib.oracle_sample_topp.argtypes = [P, P, ctypes.c_int32, ctypes.c_double, ctypes.c_double, ctypes.c_double,
+                                       P, P, P]
     lib.oracle_num_threads.restype = ctypes.c_int
     lib.oracle_set_num_threads.argtypes = [ctypes.c_int]
     _lib = lib
@@ -201,6 +203,23 @@ def topk(y: np.ndarray, k: int) -> np.ndarray:
     if rc:
         raise ValueError(f"oracle_topk failed ({rc})")
     return out
+
+
+def sample_topp(z, idx, T: float, top_p: float, u: float):
+    """(token, nucleus size, prefix sums of the weights) for one row of k
+    sorted pairs: softmax at temperature T over z, top-p nucleus, inverse-CDF
+    draw with the uniform u (oracle_sample_topp)."""
+    z = np.ascontiguousarray(z, dtype=np.float64).reshape(-1)
+    idx = np.ascontiguousarray(idx, dtype=np.int32).reshape(-1)
+    k = z.size
+    cum = np.empty(k, dtype=np.float64)
+    tok = np.zeros(1, dtype=np.int32)
+    nuc = np.zeros(1, dtype=np.int32)
+    rc = _load().oracle_sample_topp(_ptr(z), _ptr(idx), k, float(T), float(top_p), float(u), _ptr(tok), _ptr(nuc),
+                                    _ptr(cum))
+    if rc:
+        raise ValueError(f"oracle_sample_topp failed ({rc})")
+    return int(tok[0]), int(nuc[0]), cum
 
 
 # --------------------------------------------------------------------------

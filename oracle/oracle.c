@@ -401,6 +401,44 @@ int oracle_topk(const double* y, int64_t n, int32_t k, int32_t* out_idx) {
     return 0;
 }
 
+/* ------------------------------------------------------------------ */
+/* Token selection from the k selected pairs (values z[0..k) sorted,
+ * largest first; idx the matching vocabulary indices), [roadmap K5: top-k40
+ * and top-p tokens selected on the device after the tied projection].
+ * Reading: softmax over the k soft-capped values at temperature T, the
+ * nucleus is the smallest prefix whose probability reaches top_p, and the
+ * token is drawn by inverse CDF within the nucleus from the caller's uniform
+ * u in [0, 1).  NaN values weigh 0; if every weight is 0 the first pair is
+ * taken.  cum[0..k) receives the prefix sums of the weights (float64), so a
+ * caller can see how far u and top_p lie from a decision boundary.
+ * Pinned by tests/test_oracle_sample.py (hand-computed two- and three-way
+ * cases, k = 1, top_p = 1, flat weights, NaN weights). */
+int oracle_sample_topp(const double* z, const int32_t* idx, int32_t k, double T, double top_p, double u,
+                       int32_t* token, int32_t* nucleus, double* cum) {
+    if (k < 1 || !(T > 0.0) || !(top_p > 0.0) || !(top_p <= 1.0)) return 1;
+    double s = 0.0;
+    for (int32_t i = 0; i < k; ++i) {
+        const double w = (isnan(z[i]) || isnan(z[0])) ? 0.0 : exp((z[i] - z[0]) / T);
+        s += w;
+        cum[i] = s;
+    }
+    int32_t n = 1, j = 0;
+    if (s > 0.0) {
+        n = k;
+        for (int32_t i = 0; i < k; ++i) {
+            if (cum[i] >= top_p * s) { n = i + 1; break; }
+        }
+        const double target = u * cum[n - 1];
+        j = n - 1;
+        for (int32_t i = 0; i < n; ++i) {
+            if (cum[i] > target) { j = i; break; }
+        }
+    }
+    *token = idx[j];
+    *nucleus = n;
+    return 0;
+}
+
 int oracle_num_threads(void) {
 #ifdef _OPENMP
     return omp_get_max_threads();

@@ -156,6 +156,36 @@ int logits_topk(const void* W_q8_0, const float* x, float* top_val, int32_t* top
     return launched(qmv::launch_topk(y, top_val, top_idx, N, M, k, softcap, ws, stream));
 }
 
+static int check_sample_args(const float* u, const int32_t* token, const int32_t* nucleus, float temperature,
+                             float top_p) {
+    if (!u || !token || !nucleus) return QMV_ERR_NULL;
+    if (!(temperature > 0.0f) || !(temperature <= 3.4028234663852886e38f)) return QMV_ERR_ARG;
+    if (!(top_p > 0.0f) || !(top_p <= 1.0f)) return QMV_ERR_ARG;
+    if (!aligned(u, 4) || !aligned(token, 4) || !aligned(nucleus, 4)) return QMV_ERR_ALIGN;
+    return QMV_OK;
+}
+
+int logits_sample(const void* W_q8_0, const float* x, const float* u, int32_t* token, int32_t* nucleus,
+                  float* top_val, int32_t* top_idx, int64_t N, int64_t K, int64_t M, int32_t k, float softcap,
+                  float temperature, float top_p, void* ws, size_t ws_bytes, hipStream_t stream) {
+    if (!W_q8_0 || !x) return QMV_ERR_NULL;
+    int rc = check_shape(N, K, M, 32, 34);
+    if (rc) return rc;
+    rc = check_topk_args(N, M, k, softcap, top_val, top_idx, ws, ws_bytes);
+    if (rc) return rc;
+    rc = check_sample_args(u, token, nucleus, temperature, top_p);
+    if (rc) return rc;
+    if (!aligned(W_q8_0, 16) || !aligned(x, 4)) return QMV_ERR_ALIGN;
+    float* y = static_cast<float*>(ws);
+    for (int64_t m = 0; m < M; ++m) {
+        rc = launched(qmv::launch_gemv(1, W_q8_0, nullptr, x + m * K, y + m * N, N, K, stream));
+        if (rc) return rc;
+    }
+    rc = launched(qmv::launch_topk(y, top_val, top_idx, N, M, k, softcap, ws, stream));
+    if (rc) return rc;
+    return launched(qmv::launch_sample(top_val, top_idx, u, token, nucleus, M, k, temperature, top_p, stream));
+}
+
 int qmvdbg_quantize_q8(const float* x, int8_t* q, float* d, int64_t K, int64_t M, hipStream_t stream) {
     if (!x || !q || !d) return QMV_ERR_NULL;
     if (K < 32 || K % 32 != 0 || M < 1 || K > kMaxN) return QMV_ERR_SHAPE;
@@ -184,6 +214,17 @@ int qmvdbg_topk_f32(const float* y, float* top_val, int32_t* top_idx, int64_t N,
     if (rc) return rc;
     if (!aligned(y, 4)) return QMV_ERR_ALIGN;
     return launched(qmv::launch_topk(y, top_val, top_idx, N, M, k, softcap, ws, stream));
+}
+
+int qmvdbg_sample_f32(const float* top_val, const int32_t* top_idx, const float* u, int32_t* token, int32_t* nucleus,
+                      int64_t M, int32_t k, float temperature, float top_p, hipStream_t stream) {
+    if (!top_val || !top_idx) return QMV_ERR_NULL;
+    if (M < 1 || M > 65535) return QMV_ERR_SHAPE;
+    if (k < 1 || k > 64) return QMV_ERR_ARG;
+    int rc = check_sample_args(u, token, nucleus, temperature, top_p);
+    if (rc) return rc;
+    if (!aligned(top_val, 4) || !aligned(top_idx, 4)) return QMV_ERR_ALIGN;
+    return launched(qmv::launch_sample(top_val, top_idx, u, token, nucleus, M, k, temperature, top_p, stream));
 }
 
 }  // extern "C"

@@ -23,6 +23,11 @@ size_t topk_ws_bytes(int64_t N, int64_t M, int k);
 hipError_t launch_topk(const float* y, float* top_val, int32_t* top_idx, int64_t N, int64_t M,
                        int k, float softcap, void* ws, hipStream_t stream);
 
+// One token per row from the k selected pairs (top-p with temperature, the
+// caller's uniform numbers u[M]).
+hipError_t launch_sample(const float* top_val, const int32_t* top_idx, const float* u, int32_t* token,
+                         int32_t* nucleus, int64_t M, int k, float temperature, float top_p, hipStream_t stream);
+
 // Q4_0 x Q8 activations.  The workspace layout (and its size) depends on
 // (N, K, M) only.
 size_t qmm_ws_bytes(int64_t N, int64_t K, int64_t M);

@@ -18,10 +18,12 @@
 //          reduction, with no workgroup barrier.  KPL grows with N so that
 //          there are at most 1024 chunks.
 // Stage 2: one 1024-thread workgroup per activation row runs a tournament
-//          over the sorted chunk lists: thread t holds the head of list t
-//          (and the next few entries in registers); each round finds the
-//          workgroup maximum, and the thread that owned it moves to its next
-//          entry.  Keys are unique, so exactly one thread wins a round.
+//          over the sorted chunk lists in two levels: thread t holds the head
+//          of list t (and the next few entries in registers); each wave takes
+//          the k best of its 64 lists (a wave maximum per round, the lane that
+//          owned it moves to its next entry: keys are unique, so exactly one
+//          lane wins a round), then wave 0 takes the k best of the 16 wave
+//          lists the same way.  No round needs a workgroup barrier.
 // Very long rows (more than 4M entries, so more than 1024 chunks of 4096)
 // fall back to a merge that rescans candidates from memory every round.
 #include <stdint.h>
@@ -130,8 +132,10 @@ __global__ __launch_bounds__(kMergeThreads)
 void topk_tournament_kernel(const float* __restrict__ y, int64_t N, int k, int nlists, float softcap,
                             const uint64_t* __restrict__ cand, float* __restrict__ top_val,
                             int32_t* __restrict__ top_idx) {
-    __shared__ uint64_t wbest[kMergeWaves];
-    __shared__ uint64_t won[64];
+    // Round 1: every wave runs its own tournament over its 64 lists (a wave
+    // maximum per round, no workgroup barrier) and keeps its k winners in
+    // LDS.  Round 2: wave 0 runs the tournament over the 16 waves' lists.
+    __shared__ uint64_t wlist[kMergeWaves][64];
     const int m = blockIdx.x;
     const int t = threadIdx.x;
     const int w = t / kWave;
@@ -143,30 +147,44 @@ void topk_tournament_kernel(const float* __restrict__ y, int64_t N, int k, int n
     for (int i = 0; i < kListRegs; ++i) buf[i] = (mine && i < k) ? list[i] : 0ull;
     int next = kListRegs;  // next entry of the list to fetch
     for (int r = 0; r < k; ++r) {
-        const uint64_t wb = wave_max64(buf[0]);
-        if (lane == 0) wbest[w] = wb;
-        __syncthreads();
-        uint64_t g = lane < kMergeWaves ? wbest[lane] : 0ull;
-        g = wave_max64(g);
-        if (t == 0) won[r] = g;
-        __syncthreads();  // wbest is rewritten next round
-        if (buf[0] == g && g != 0ull) {  // keys are unique: one thread
+        const uint64_t g = wave_max64(buf[0]);
+        if (lane == 0) wlist[w][r] = g;
+        if (buf[0] == g && g != 0ull) {  // keys are unique: one lane
 #pragma unroll
             for (int i = 0; i + 1 < kListRegs; ++i) buf[i] = buf[i + 1];
-            buf[kListRegs - 1] = (next < k) ? list[next] : 0ull;
-            ++next;
+            buf[kListRegs - 1] = 0ull;
+            // Refill only when the register copy runs dry: a load issued every
+            // round would make the next round wait for it (the wait counts
+            // are per wave), and a list rarely gives more than a few winners.
+            if (buf[0] == 0ull && next < k) {
+#pragma unroll
+                for (int i = 0; i < kListRegs; ++i) buf[i] = (next + i < k) ? list[next + i] : 0ull;
+                next += kListRegs;
+            }
         }
     }
     __syncthreads();
-    if (t < k) {
+    if (w != 0) return;
+    int pos = 0;  // lane l < 16 reads wave l's list
+    uint64_t head = lane < kMergeWaves ? wlist[lane][0] : 0ull;
+    uint64_t mine_key = 0ull;  // lane r keeps the winner of round r
+    for (int r = 0; r < k; ++r) {
+        const uint64_t g = wave_max64(head);
+        if (lane == r) mine_key = g;
+        if (head == g && g != 0ull) {
+            ++pos;
+            head = pos < k ? wlist[lane][pos] : 0ull;
+        }
+    }
+    if (lane < k) {
         // k <= N guarantees a real key every round; a zero key would mean
         // "nothing left" and is never dereferenced.
-        const uint64_t g = won[t];
+        const uint64_t g = mine_key;
         const uint32_t idx = 0xFFFFFFFFu - static_cast<uint32_t>(g);
         const bool real = g != 0ull && idx < static_cast<uint64_t>(N);
         const float v = real ? y[static_cast<int64_t>(m) * N + idx] : __builtin_nanf("");
-        top_idx[static_cast<int64_t>(m) * k + t] = real ? static_cast<int32_t>(idx) : -1;
-        top_val[static_cast<int64_t>(m) * k + t] = softcap * tanhf(v / softcap);
+        top_idx[static_cast<int64_t>(m) * k + lane] = real ? static_cast<int32_t>(idx) : -1;
+        top_val[static_cast<int64_t>(m) * k + lane] = softcap * tanhf(v / softcap);
     }
 }
 
@@ -231,6 +249,49 @@ int64_t wave_chunks_of(int64_t N) {
 
 size_t align256(size_t b) { return (b + 255) & ~static_cast<size_t>(255); }
 
+// ---------------------------------------------------------- sampling
+// One wave per row draws a token from the k selected (value, index) pairs
+// ["Gemma 4 M4 Max kernel roadmap", K5: top-k40 / top-p token selection on
+// the device after the tied projection]:
+//   w_i = exp((z_i - z_0) / T) for i < k (z sorted, largest first; NaN -> 0),
+//   n   = the smallest count whose prefix sum reaches top_p * sum(w)  (n >= 1),
+//   j   = the first i < n whose prefix sum exceeds u * (prefix sum of n),
+//   token = index_j.
+// Lane i holds candidate i; the prefix sums are one inclusive wave scan (a
+// fixed order, so the draw is reproducible).
+__global__ __launch_bounds__(kWave)
+void sample_topp_kernel(const float* __restrict__ top_val, const int32_t* __restrict__ top_idx,
+                        const float* __restrict__ u, int32_t* __restrict__ token, int32_t* __restrict__ nucleus,
+                        int k, float temperature, float top_p) {
+    const int64_t m = blockIdx.x;
+    const int lane = threadIdx.x;
+    const bool have = lane < k;
+    const float z = have ? top_val[m * k + lane] : 0.0f;
+    const float z0 = __shfl(z, 0, kWave);
+    float w = 0.0f;
+    if (have && z == z && z0 == z0) w = expf((z - z0) / temperature);
+    float cum = w;
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+        const float t = __shfl_up(cum, o, kWave);
+        if (lane >= o) cum += t;
+    }
+    const float total = __shfl(cum, kWave - 1, kWave);
+    int n = 1, j = 0;
+    if (total > 0.0f) {
+        const uint64_t reach = __ballot(have && cum >= top_p * total);
+        n = reach ? __ffsll(static_cast<unsigned long long>(reach)) : k;  // first lane reaching, plus one
+        const float cut = __shfl(cum, n - 1, kWave);
+        const float target = u[m] * cut;
+        const uint64_t past = __ballot(lane < n && cum > target);
+        j = past ? __ffsll(static_cast<unsigned long long>(past)) - 1 : n - 1;
+    }
+    if (lane == 0) {
+        token[m] = top_idx[m * k + j];
+        nucleus[m] = n;
+    }
+}
+
 }  // namespace
 
 size_t topk_ws_bytes(int64_t N, int64_t M, int k) {
@@ -267,6 +328,13 @@ hipError_t launch_topk(const float* y, float* top_val, int32_t* top_idx, int64_t
         hipLaunchKernelGGL(topk_merge_scan_kernel, dim3(static_cast<unsigned>(M)), dim3(kMergeThreads), 0, stream,
                            y, N, k, nwchunks, softcap, cand, top_val, top_idx);
     }
+    return hipGetLastError();
+}
+
+hipError_t launch_sample(const float* top_val, const int32_t* top_idx, const float* u, int32_t* token,
+                         int32_t* nucleus, int64_t M, int k, float temperature, float top_p, hipStream_t stream) {
+    hipLaunchKernelGGL(sample_topp_kernel, dim3(static_cast<unsigned>(M)), dim3(kWave), 0, stream, top_val, top_idx, u,
+                       token, nucleus, k, temperature, top_p);
     return hipGetLastError();
 }
 

@@ -37,9 +37,11 @@ _SIGS = {
     "qmm_q4_0_f32act": ([_P, _P, _P, _I64, _I64, _I64, _P, _SZ, _P], ctypes.c_int),
     "logits_topk_ws_bytes": ([_I64, _I64, _I32], _SZ),
     "logits_topk": ([_P, _P, _P, _P, _I64, _I64, _I64, _I32, _F, _P, _SZ, _P], ctypes.c_int),
+    "logits_sample": ([_P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I32, _F, _F, _F, _P, _SZ, _P], ctypes.c_int),
     "qmvdbg_quantize_q8": ([_P, _P, _P, _I64, _I64, _P], ctypes.c_int),
     "qmvdbg_q4_0_q8_blocksums": ([_P, _P, _P, _I64, _I64, _I64, _P], ctypes.c_int),
     "qmvdbg_topk_f32": ([_P, _P, _P, _I64, _I64, _I32, _F, _P, _SZ, _P], ctypes.c_int),
+    "qmvdbg_sample_f32": ([_P, _P, _P, _P, _P, _I64, _I32, _F, _F, _P], ctypes.c_int),
 }
 for _name, (_args, _res) in _SIGS.items():
     _fn = getattr(lib, _name)
@@ -135,3 +137,14 @@ def qmvdbg_q4_0_q8_blocksums(W, qx, isum, N, K, M, stream=None):
 def qmvdbg_topk_f32(y, top_val, top_idx, N, M, k, softcap, ws, ws_bytes, stream=None):
     _call("qmvdbg_topk_f32", _ptr(y), _ptr(top_val), _ptr(top_idx), N, M, k, softcap, _ptr(ws), ws_bytes,
           _stream(stream))
+
+
+def logits_sample(W_q8_0, x, u, token, nucleus, top_val, top_idx, N, K, M, k, softcap, temperature, top_p, ws,
+                  ws_bytes, stream=None):
+    _call("logits_sample", _ptr(W_q8_0), _ptr(x), _ptr(u), _ptr(token), _ptr(nucleus), _ptr(top_val),
+          _ptr(top_idx), N, K, M, k, softcap, temperature, top_p, _ptr(ws), ws_bytes, _stream(stream))
+
+
+def qmvdbg_sample_f32(top_val, top_idx, u, token, nucleus, M, k, temperature, top_p, stream=None):
+    _call("qmvdbg_sample_f32", _ptr(top_val), _ptr(top_idx), _ptr(u), _ptr(token), _ptr(nucleus), M, k,
+          temperature, top_p, _stream(stream))

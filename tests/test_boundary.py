@@ -26,7 +26,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported_and_bound():
     names = declared_functions()
-    assert "qmv_q4_0" in names and "logits_topk" in names and len(names) == 14
+    assert "qmv_q4_0" in names and "logits_topk" in names and len(names) == 16
     for n in names:
         assert hasattr(qmv.lib, n), n
     assert sorted(qmv.EXPORTS) == names
@@ -145,6 +145,37 @@ def test_logits_topk_validation():
     assert run(i=FAKE + 2) == ALIGN
     assert run(K=48) == SHAPE
     assert run(M=70000) == SHAPE
+
+
+def test_logits_sample_validation():
+    args = lambda **kw: dict(dict(W=FAKE, x=FAKE, u=FAKE, t=FAKE, n=FAKE, v=FAKE, i=FAKE, N=1000, K=64, M=1,
+                                  k=40, cap=30.0, T=1.0, p=0.9, ws=FAKE, wsb=1 << 30), **kw)
+
+    def run(**kw):
+        a = args(**kw)
+        return call("logits_sample", a["W"], a["x"], a["u"], a["t"], a["n"], a["v"], a["i"], a["N"], a["K"],
+                    a["M"], a["k"], a["cap"], a["T"], a["p"], a["ws"], a["wsb"], S)
+
+    assert run(u=None) == NUL
+    assert run(t=None) == NUL
+    assert run(n=None) == NUL
+    assert run(W=None) == NUL
+    assert run(T=0.0) == ARG
+    assert run(T=float("inf")) == ARG
+    assert run(T=float("nan")) == ARG
+    assert run(p=0.0) == ARG
+    assert run(p=1.5) == ARG
+    assert run(p=float("nan")) == ARG
+    assert run(k=65) == ARG
+    assert run(u=FAKE + 2) == ALIGN
+    assert run(t=FAKE + 1) == ALIGN
+    assert run(wsb=16) == WS
+    assert run(K=48) == SHAPE
+    assert call("qmvdbg_sample_f32", FAKE, FAKE, FAKE, FAKE, FAKE, 1, 65, 1.0, 0.9, S) == ARG
+    assert call("qmvdbg_sample_f32", FAKE, FAKE, FAKE, FAKE, FAKE, 0, 10, 1.0, 0.9, S) == SHAPE
+    assert call("qmvdbg_sample_f32", FAKE, None, FAKE, FAKE, FAKE, 1, 10, 1.0, 0.9, S) == NUL
+    assert call("qmvdbg_sample_f32", FAKE, FAKE, FAKE, FAKE, FAKE, 1, 10, -1.0, 0.9, S) == ARG
+    assert call("qmvdbg_sample_f32", FAKE + 1, FAKE, FAKE, FAKE, FAKE, 1, 10, 1.0, 0.9, S) == ALIGN
 
 
 def test_debug_entry_validation():
