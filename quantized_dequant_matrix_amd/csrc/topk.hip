@@ -76,10 +76,19 @@ __device__ __forceinline__ uint32_t wave_max32(uint32_t v) {
 
 // Maximum of a 64-bit key over the wave: the largest high word first, then
 // the largest low word among the lanes that hold it (two 32-bit reductions
-// are shorter dependent chains than one on 64-bit values).
+// are shorter dependent chains than one on 64-bit values).  When a single
+// lane holds the largest high word (equal values are rare), its low word is
+// read directly and the second reduction is skipped.
 __device__ __forceinline__ uint64_t wave_max64(uint64_t v) {
     const uint32_t hi = wave_max32(static_cast<uint32_t>(v >> 32));
-    const uint32_t lo = wave_max32(static_cast<uint32_t>(v >> 32) == hi ? static_cast<uint32_t>(v) : 0u);
+    const uint64_t holders = __ballot(static_cast<uint32_t>(v >> 32) == hi);
+    uint32_t lo;
+    if (__popcll(holders) == 1) {
+        lo = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(static_cast<uint32_t>(v)),
+                                                             __ffsll(static_cast<unsigned long long>(holders)) - 1));
+    } else {
+        lo = wave_max32(static_cast<uint32_t>(v >> 32) == hi ? static_cast<uint32_t>(v) : 0u);
+    }
     return (static_cast<uint64_t>(hi) << 32) | lo;
 }
 
