@@ -20,8 +20,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
 
-Q4_0, Q8_0, Q4_K = 0, 1, 2
-FORMATS = {"q4_0": Q4_0, "q8_0": Q8_0, "q4_k": Q4_K}
+Q4_0, Q8_0, Q4_K, Q6_K = 0, 1, 2, 3
+FORMATS = {"q4_0": Q4_0, "q8_0": Q8_0, "q4_k": Q4_K, "q6_k": Q6_K}
 
 _lib = None
 
@@ -57,6 +57,7 @@ def _load():
     lib.oracle_gelu_tanh.argtypes = [ctypes.c_double]
     lib.oracle_gelu_tanh.restype = ctypes.c_double
     lib.oracle_geglu.argtypes = [P, P, I64, P]
+    lib.oracle_qmv_geglu_down.argtypes = [ctypes.c_int, P, I64, I64, P, P, I64, P, I64, P, P, P]
     lib.oracle_softcap.argtypes = [P, I64, ctypes.c_double, P]
     lib.oracle_quantize_q8.argtypes = [P, I64, I64, P, P]
     lib.oracle_q4_0_q8_blocksums.argtypes = [P, I64, I64, P, I64, P, I64, P]
@@ -147,6 +148,25 @@ def geglu(g: np.ndarray, u: np.ndarray) -> np.ndarray:
     return h
 
 
+def qmv_geglu_down(fmt: str, W: np.ndarray, N: int, K: int, g: np.ndarray, u: np.ndarray, M: int = 1, rows=None):
+    """float64 y[M, nrows] = W (gelu(g) * u), with S = sum |w h| and
+    E = sum |w| |u| (|g| + |gelu(g)|) for the selected rows."""
+    W = np.ascontiguousarray(W).view(np.uint8).reshape(-1)
+    g = np.ascontiguousarray(g, dtype=np.float32).reshape(-1)
+    u = np.ascontiguousarray(u, dtype=np.float32).reshape(-1)
+    if W.size != N * row_bytes(fmt, K) or g.size != M * K or u.size != M * K:
+        raise ValueError("shape mismatch")
+    r, nrows = _rows_arg(rows, N)
+    y = np.empty((M, nrows), dtype=np.float64)
+    S = np.empty((M, nrows), dtype=np.float64)
+    E = np.empty((M, nrows), dtype=np.float64)
+    rc = _load().oracle_qmv_geglu_down(FORMATS[fmt], _ptr(W), N, K, _ptr(g), _ptr(u), M,
+                                       None if r is None else _ptr(r), nrows, _ptr(y), _ptr(S), _ptr(E))
+    if rc:
+        raise ValueError(f"oracle_qmv_geglu_down failed ({rc})")
+    return y, S, E
+
+
 def softcap(y: np.ndarray, cap: float) -> np.ndarray:
     y = np.ascontiguousarray(y, dtype=np.float64).reshape(-1)
     z = np.empty_like(y)
@@ -232,6 +252,21 @@ ABS_TOL = 1e-6
 
 def float_tol(S: np.ndarray) -> np.ndarray:
     return REL_TOL * np.asarray(S, dtype=np.float64) + ABS_TOL
+
+
+# float32 evaluation of h = gelu(g) * u: |dh| <= 2^-20 |u| (|g| + |gelu(g)|).
+# The inner polynomial has no cancellation (v and 0.044715 v^3 share a sign),
+# so it carries a few float32 roundings; tanhf adds a couple of ulps and at
+# most 0.45 times the inner's relative error; 1 + t, the two products and the
+# factor 1/2 add a few more: about 8 units of 2^-24 on |g| |u| and 2 on |h|.
+# 2^-20 = 16 units leaves a factor-2 margin over that count.
+H_F32_REL = 2.0**-20
+
+
+def geglu_down_tol(S, E):
+    """|y - y_ref| <= 1e-5 S + 2^-20 E + 1e-6 for y = W (gelu(g) * u): the
+    linear bound on the products, plus the propagated float32 error of h."""
+    return float_tol(S) + H_F32_REL * np.asarray(E, dtype=np.float64)
 
 
 def geglu_tol(g_ref, u_ref, Sg, Su, h_ref):

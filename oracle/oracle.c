@@ -36,6 +36,7 @@
 #define ORACLE_Q4_0 0
 #define ORACLE_Q8_0 1
 #define ORACLE_Q4_K 2
+#define ORACLE_Q6_K 3
 
 /* ------------------------------------------------------------------ */
 /* IEEE 754 binary16 -> double.                                        */
@@ -67,6 +68,7 @@ int64_t oracle_row_bytes(int fmt, int64_t K) {
     case ORACLE_Q4_0: return (K % 32) ? -1 : (K / 32) * 18;
     case ORACLE_Q8_0: return (K % 32) ? -1 : (K / 32) * 34;
     case ORACLE_Q4_K: return (K % 256) ? -1 : (K / 256) * 144;
+    case ORACLE_Q6_K: return (K % 256) ? -1 : (K / 256) * 210;
     default: return -1;
     }
 }
@@ -138,6 +140,36 @@ static void dequant_q4_k_block(const uint8_t* b, double* w) {
     }
 }
 
+/* Q6_K super-block (210 B, 256 weights) [captable section 1, q6k_matvec:
+ * "Q6_K 210B planar"; the format of the V and down projections in the
+ * pages' Q4_K_M mix, captable section 2 q4k_q6k_qkv_proj]:
+ *   bytes 0-127 ql (low 4 bits of the codes), 128-191 qh (high 2 bits),
+ *   192-207 sixteen signed 8-bit sub-block scales, 208-209 d (fp16).
+ * Reading (the pages give the size and the word "planar" only; the GGUF
+ * super-block is what their loaders read):
+ *   element e = 128h + 32g + l (h < 2, g < 4, l < 32) takes
+ *     the low nibble (g = 0, 1) or the high nibble (g = 2, 3) of
+ *     ql[64h + 32(g mod 2) + l], and bits 2g, 2g+1 of qh[32h + l] as its
+ *     two high bits;  q = nibble + 16 * high bits, in 0..63;
+ *   w_e = d * scale[e / 16] * (q - 32).
+ * Pinned by hand-built super-blocks (q = 32 -> 0, 0 -> -32 d s,
+ * 63 -> 31 d s, signed scales -128 and 127, every element placed alone) in
+ * tests/test_oracle_formats.py. */
+static void dequant_q6_k_block(const uint8_t* b, double* w) {
+    const uint8_t* ql = b;
+    const uint8_t* qh = b + 128;
+    const int8_t* sc = (const int8_t*)(b + 192);
+    double d = oracle_fp16_to_f64(rd16(b + 208));
+    for (int e = 0; e < 256; ++e) {
+        int h = e / 128, g = (e % 128) / 32, l = e % 32;
+        uint8_t lowbyte = ql[64 * h + 32 * (g % 2) + l];
+        int nib = (g < 2) ? (lowbyte & 0x0f) : (lowbyte >> 4);
+        int high = (qh[32 * h + l] >> (2 * g)) & 3;
+        int q = nib + 16 * high;
+        w[e] = d * (double)sc[e / 16] * (double)(q - 32);
+    }
+}
+
 /* Dequantize one row of K weights to float64.  Returns 0, or -1 on a bad
  * format / K. */
 int oracle_dequant_row(int fmt, const uint8_t* row, int64_t K, double* w) {
@@ -146,8 +178,10 @@ int oracle_dequant_row(int fmt, const uint8_t* row, int64_t K, double* w) {
         for (int64_t b = 0; b < K / 32; ++b) dequant_q4_0_block(row + 18 * b, w + 32 * b);
     } else if (fmt == ORACLE_Q8_0) {
         for (int64_t b = 0; b < K / 32; ++b) dequant_q8_0_block(row + 34 * b, w + 32 * b);
-    } else {
+    } else if (fmt == ORACLE_Q4_K) {
         for (int64_t b = 0; b < K / 256; ++b) dequant_q4_k_block(row + 144 * b, w + 256 * b);
+    } else {
+        for (int64_t b = 0; b < K / 256; ++b) dequant_q6_k_block(row + 210 * b, w + 256 * b);
     }
     return 0;
 }
@@ -223,6 +257,74 @@ double oracle_gelu_tanh(double v) {
 /* Gated pair: h = gelu(g) * u   [roadmap K2 step 5: gated GELU FFN projection pair] */
 void oracle_geglu(const double* g, const double* u, int64_t n, double* h) {
     for (int64_t i = 0; i < n; ++i) h[i] = oracle_gelu_tanh(g[i]) * u[i];
+}
+
+/* ------------------------------------------------------------------ */
+/* Down projection of a gated FFN with the GELU gate applied to its     */
+/* input [captable section 4: q4k_geglu_gelu_tanh_down and              */
+/* q6k_geglu_gelu_tanh_down take the gate and up activations and fold   */
+/* the GELU-tanh product into the down matrix-vector; roadmap K2 step 5: */
+/* the gated GELU FFN]:                                                 */
+/*   h[m][k] = gelu(g[m][k]) * u[m][k]             (float64)            */
+/*   y[m][i] = sum_k w[r_i][k] * h[m][k]           (naive, k ascending) */
+/*   S[m][i] = sum_k |w[r_i][k] * h[m][k]|                              */
+/*   E[m][i] = sum_k |w[r_i][k]| |u[m][k]| (|g[m][k]| + |gelu(g[m][k])|) */
+/* E scales the error a float32 evaluation of h may add (the tolerance  */
+/* rule in __init__.py).                                                */
+/* Pinned in tests/test_oracle_geglu_down.py by gates of +-64 (gelu     */
+/* exactly 64 or -0 in float64, so y = 64 W u exactly or 0), u = 0, and */
+/* the agreement of S and E with qmv's S at those gates.                */
+/* ------------------------------------------------------------------ */
+int oracle_qmv_geglu_down(int fmt, const uint8_t* W, int64_t N, int64_t K,
+                          const float* g, const float* u, int64_t M,
+                          const int64_t* rows, int64_t nrows,
+                          double* y, double* S, double* E) {
+    int64_t rb = oracle_row_bytes(fmt, K);
+    if (rb < 0) return -1;
+    if (rows == NULL) nrows = N;
+    for (int64_t i = 0; i < nrows; ++i) {
+        int64_t r = rows ? rows[i] : i;
+        if (r < 0 || r >= N) return -2;
+    }
+    double* h = (double*)malloc(sizeof(double) * (size_t)(M * K));
+    double* e = (double*)malloc(sizeof(double) * (size_t)(M * K));
+    if (!h || !e) { free(h); free(e); return -3; }
+    for (int64_t t = 0; t < M * K; ++t) {
+        double gl = oracle_gelu_tanh((double)g[t]);
+        h[t] = gl * (double)u[t];
+        e[t] = fabs((double)u[t]) * (fabs((double)g[t]) + fabs(gl));
+    }
+    int bad = 0;
+#pragma omp parallel
+    {
+        double* w = (double*)malloc(sizeof(double) * (size_t)K);
+        if (!w) {
+#pragma omp atomic write
+            bad = 1;
+        }
+#pragma omp for schedule(static)
+        for (int64_t i = 0; i < nrows; ++i) {
+            if (!w) continue;
+            int64_t r = rows ? rows[i] : i;
+            oracle_dequant_row(fmt, W + r * rb, K, w);
+            for (int64_t m = 0; m < M; ++m) {
+                double acc = 0.0, sabs = 0.0, eabs = 0.0;
+                for (int64_t k = 0; k < K; ++k) {
+                    double p = w[k] * h[m * K + k];
+                    acc += p;
+                    sabs += fabs(p);
+                    eabs += fabs(w[k]) * e[m * K + k];
+                }
+                y[m * nrows + i] = acc;
+                if (S) S[m * nrows + i] = sabs;
+                if (E) E[m * nrows + i] = eabs;
+            }
+        }
+        free(w);
+    }
+    free(h);
+    free(e);
+    return bad ? -3 : 0;
 }
 
 /* Logit soft-cap z = cap * tanh(y / cap), float64.                     */

@@ -1,5 +1,5 @@
-"""Seeded synthetic inputs: packed Q4_0 / Q8_0 / Q4_K weight bytes and f32
-activations.
+"""Seeded synthetic inputs: packed Q4_0 / Q8_0 / Q4_K / Q6_K weight bytes and
+f32 activations.
 
 This module only draws random numbers and lays them out in the block
 formats' byte layout; it holds none of the arithmetic of the method (no
@@ -9,13 +9,16 @@ the very same bytes, so a reader can regenerate any test input from its seed.
 Generator: numpy PCG64, one seed per workload.  Draw order inside one call:
 block scales first (all blocks, row-major), then the code bytes (all blocks,
 row-major), then the extra Q4_K fields (dmin, sub-block scales, sub-block
-mins), and finally the activations.
+mins) or Q6_K fields (sub-block scales), and finally the activations.
 
 Value distributions (the synthetic stand-ins for real model weights):
   Q4_0: d = fp16(|N(0,1)| * 0.02), q uniform in 0..15     (w = (q - 8) d)
   Q8_0: d = fp16(|N(0,1)| * 0.01), q uniform in -127..127 (w = q d)
   Q4_K: d, dmin = fp16(|N(0,1)| * 0.01), sub-block scales and mins uniform
         in 0..63, q uniform in 0..15
+  Q6_K: d = fp16(|N(0,1)| * 0.0001) (about half of them fp16 subnormals,
+        as in real Q6_K tensors), sub-block scales uniform int8 in
+        -128..127, 6-bit q uniform in 0..63 (w = d s (q - 32))
   x:    f32 ~ N(0,1)
 N(0,1) is drawn in float32, scaled in float32 and rounded to fp16 by numpy
 (round to nearest even, subnormals kept).  4-bit codes are drawn as whole
@@ -29,13 +32,16 @@ Byte layouts (GGUF block formats, as loaded by the pages' engines):
   Q8_0 (34 B / 32): fp16 d | 32 int8
   Q4_K (144 B / 256): fp16 d | fp16 dmin | 12 bytes of 6-bit scales/mins |
         128 code bytes; byte 32c+l = q[64c+l] | q[64c+32+l] << 4
+  Q6_K (210 B / 256): 128 bytes ql | 64 bytes qh | 16 int8 scales | fp16 d;
+        element 128h+32g+l: low (g < 2) or high (g >= 2) nibble of
+        ql[64h+32(g%2)+l], two high bits at bits 2g, 2g+1 of qh[32h+l]
 """
 from __future__ import annotations
 
 import numpy as np
 
-BLOCK_BYTES = {"q4_0": 18, "q8_0": 34, "q4_k": 144}
-BLOCK_ELEMS = {"q4_0": 32, "q8_0": 32, "q4_k": 256}
+BLOCK_BYTES = {"q4_0": 18, "q8_0": 34, "q4_k": 144, "q6_k": 210}
+BLOCK_ELEMS = {"q4_0": 32, "q8_0": 32, "q4_k": 256, "q6_k": 256}
 
 # Seeds of the five workloads; the up-projection matrix of the gated pair
 # uses its own seed.
@@ -103,6 +109,24 @@ def pack_q4_k(d, dmin, sc, mn, q) -> np.ndarray:
     return out.reshape(-1)
 
 
+def pack_q6_k(d, sc, q) -> np.ndarray:
+    """d: float16[nb]; sc: int8[nb, 16]; q: uint8[nb, 256] in 0..63 -> uint8[nb*210]."""
+    nb = d.size
+    q = np.asarray(q, dtype=np.uint8).reshape(nb, 2, 4, 32)  # [block, h, g, l]
+    lo = q & 15
+    hi = (q >> 4) & 3
+    ql = np.empty((nb, 2, 2, 32), dtype=np.uint8)             # [block, h, g % 2, l]
+    ql[:, :, 0] = lo[:, :, 0] | (lo[:, :, 2] << 4)
+    ql[:, :, 1] = lo[:, :, 1] | (lo[:, :, 3] << 4)
+    qh = hi[:, :, 0] | (hi[:, :, 1] << 2) | (hi[:, :, 2] << 4) | (hi[:, :, 3] << 6)
+    out = np.empty((nb, 210), dtype=np.uint8)
+    out[:, 0:128] = ql.reshape(nb, 128)
+    out[:, 128:192] = qh.reshape(nb, 64)
+    out[:, 192:208] = np.ascontiguousarray(sc, dtype=np.int8).view(np.uint8).reshape(nb, 16)
+    out[:, 208:210] = np.ascontiguousarray(d, dtype=np.float16).view(np.uint8).reshape(nb, 2)
+    return out.reshape(-1)
+
+
 def _blocks(nb: int, nbytes: int) -> np.ndarray:
     return np.empty((nb, nbytes), dtype=np.uint8)
 
@@ -157,12 +181,26 @@ def q4_k_weights(N: int, K: int, seed: int, rng=None) -> np.ndarray:
     return out.reshape(-1)
 
 
+def q6_k_weights(N: int, K: int, seed: int, rng=None) -> np.ndarray:
+    rng = rng or _rng(seed)
+    row_bytes("q6_k", K)
+    nb = N * (K // 256)
+    d = _fp16_scales(rng, nb, 0.0001)
+    codes = _random_bytes(rng, (nb, 192))  # ql and qh: every 6-bit code uniform
+    sc = _random_bytes(rng, (nb, 16))
+    out = _blocks(nb, 210)
+    out[:, 0:192] = codes
+    out[:, 192:208] = sc
+    out[:, 208:210] = d.view(np.uint8).reshape(nb, 2)
+    return out.reshape(-1)
+
+
 def activations(M: int, K: int, seed: int, rng=None) -> np.ndarray:
     rng = rng or _rng(seed)
     return rng.standard_normal(M * K, dtype=np.float32).reshape(M, K)
 
 
-WEIGHTS = {"q4_0": q4_0_weights, "q8_0": q8_0_weights, "q4_k": q4_k_weights}
+WEIGHTS = {"q4_0": q4_0_weights, "q8_0": q8_0_weights, "q4_k": q4_k_weights, "q6_k": q6_k_weights}
 
 
 def problem(fmt: str, N: int, K: int, M: int, seed: int):

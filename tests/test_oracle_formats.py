@@ -194,3 +194,82 @@ def test_generator_layout_matches_decoder():
     Wk = synth.pack_q4_k(np.array([0.5], np.float16), np.array([0.25], np.float16), sc, mn, qk)
     ref = q4_k_block(0.5, 0.25, sc[0].tolist(), mn[0].tolist(), qk[0].tolist())
     assert np.array_equal(Wk, ref)
+
+
+# ---------------------------------------------------------------- Q6_K
+def q6_k_block(d: float, scales16, q256) -> np.ndarray:
+    """Q6_K super-block built by explicit bit placement: element
+    e = 128h + 32g + l puts its low 4 bits into the low (g < 2) or high
+    (g >= 2) nibble of ql byte 64h + 32(g % 2) + l, and its top 2 bits into
+    bits 2g, 2g+1 of qh byte 32h + l."""
+    ql = bytearray(128)
+    qh = bytearray(64)
+    for e in range(256):
+        h, g, l = e // 128, (e % 128) // 32, e % 32
+        q = q256[e]
+        assert 0 <= q < 64
+        i = 64 * h + 32 * (g % 2) + l
+        ql[i] |= (q & 15) << (0 if g < 2 else 4)
+        qh[32 * h + l] |= (q >> 4) << (2 * g)
+    raw = bytes(ql) + bytes(qh) + np.array(scales16, dtype=np.int8).tobytes() + _f16_bytes(d)
+    assert len(raw) == 210
+    return np.frombuffer(raw, dtype=np.uint8)
+
+
+@pytest.mark.parametrize("q,expect", [(32, 0.0), (0, -32.0), (63, 31.0), (33, 1.0), (31, -1.0), (48, 16.0)])
+def test_q6_k_code_offset(q, expect):
+    w = oracle.dequant_row("q6_k", q6_k_block(0.5, [3] * 16, [q] * 256), 256)
+    assert np.all(w == expect * 0.5 * 3)
+
+
+def test_q6_k_each_element_alone():
+    # one element at a time carries a nonzero code (all others q = 32, i.e.
+    # weight 0); the scale of its 16-element sub-block is 1 + (e // 16)
+    sc = [1 + s for s in range(16)]
+    for e in range(256):
+        q = [32] * 256
+        q[e] = 32 + 1 + (e % 31) if e % 2 else 31 - (e % 32)
+        w = oracle.dequant_row("q6_k", q6_k_block(1.0, sc, q), 256)
+        expect = np.zeros(256)
+        expect[e] = (q[e] - 32) * sc[e // 16]
+        assert np.array_equal(w, expect), f"element {e}"
+
+
+@pytest.mark.parametrize("s", [-128, -1, 1, 127])
+def test_q6_k_signed_scales(s):
+    for j in (0, 7, 15):
+        sc = [0] * 16
+        sc[j] = s
+        w = oracle.dequant_row("q6_k", q6_k_block(0.25, sc, [63] * 256), 256)
+        expect = np.zeros(256)
+        expect[16 * j:16 * j + 16] = 0.25 * s * 31
+        assert np.array_equal(w, expect)
+
+
+@pytest.mark.parametrize("dbits", [0x0000, 0x8000, 0x0001, 0x03FF, 0x0400, 0x3C00, 0x7BFF, 0xBC00])
+def test_q6_k_scale_values(dbits):
+    d = float(np.array([dbits], dtype=np.uint16).view(np.float16)[0])
+    blk = q6_k_block(d, [-128] * 16, [0] * 128 + [63] * 128)
+    w = oracle.dequant_row("q6_k", blk, 256)
+    assert w[0] == d * -128 * -32 and w[255] == d * -128 * 31
+
+
+def test_q6_k_requires_whole_superblocks():
+    assert oracle.row_bytes("q6_k", 256) == 210
+    assert oracle.row_bytes("q6_k", 5376) == 4410
+    assert oracle.row_bytes("q6_k", 288) == -1
+
+
+def test_q6_k_generator_layout_matches_decoder():
+    from quantized_dequant_matrix_amd import synth
+    rng = np.random.default_rng(12)
+    q = rng.integers(0, 64, size=(2, 256), dtype=np.uint8)
+    sc = rng.integers(-128, 128, size=(2, 16), dtype=np.int8)
+    d = np.array([0.5, -0.125], dtype=np.float16)
+    W = synth.pack_q6_k(d, sc, q)
+    ref = np.concatenate([q6_k_block(float(d[i]), sc[i].tolist(), q[i].tolist()) for i in range(2)])
+    assert np.array_equal(W, ref)
+    w = oracle.dequant_row("q6_k", W, 512)
+    expect = (d.astype(np.float64)[:, None] * np.repeat(sc.astype(np.float64), 16, axis=1)
+              * (q.astype(np.float64) - 32)).reshape(-1)
+    assert np.array_equal(w, expect)

@@ -28,6 +28,24 @@ def exact_weights(fmt: str, W: np.ndarray, N: int, K: int):
                 blk = r[34 * b:34 * b + 34]
                 d = Fraction(float(np.frombuffer(blk[:2], np.float16)[0]))
                 w += [(v - 256 if v > 127 else v) * d for v in blk[2:]]
+        elif fmt == "q6_k":
+            # byte-centric reading: each ql byte feeds two elements (its low
+            # nibble and its high nibble, 64 apart), each qh byte feeds four
+            # elements 32 apart with two bits each
+            for b in range(K // 256):
+                blk = r[210 * b:210 * b + 210]
+                d = Fraction(float(np.frombuffer(blk[208:210], np.float16)[0]))
+                q = [0] * 256
+                for i in range(128):
+                    h, rr = divmod(i, 64)
+                    q[128 * h + rr] += blk[i] % 16
+                    q[128 * h + 64 + rr] += blk[i] // 16
+                for j in range(64):
+                    h, l = divmod(j, 32)
+                    for f in range(4):
+                        q[128 * h + 32 * f + l] += ((blk[128 + j] >> (2 * f)) % 4) * 16
+                sc = [v - 256 if v > 127 else v for v in blk[192:208]]
+                w += [d * sc[e // 16] * (q[e] - 32) for e in range(256)]
         else:
             for b in range(K // 256):
                 blk = r[144 * b:144 * b + 144]
@@ -49,7 +67,8 @@ def exact_weights(fmt: str, W: np.ndarray, N: int, K: int):
     return rows
 
 
-@pytest.mark.parametrize("fmt,K", [("q4_0", 32), ("q4_0", 64), ("q8_0", 32), ("q8_0", 64), ("q4_k", 256)])
+@pytest.mark.parametrize("fmt,K", [("q4_0", 32), ("q4_0", 64), ("q8_0", 32), ("q8_0", 64), ("q4_k", 256),
+                                   ("q6_k", 256), ("q6_k", 512)])
 def test_brute_force_exact(fmt, K):
     N = 5
     W, x = synth.problem(fmt, N, K, 1, seed=1000 + K)
@@ -65,7 +84,7 @@ def test_brute_force_exact(fmt, K):
         assert abs(S[0, n] - float(sabs)) <= bound
 
 
-@pytest.mark.parametrize("fmt,K", [("q4_0", 96), ("q8_0", 64), ("q4_k", 512)])
+@pytest.mark.parametrize("fmt,K", [("q4_0", 96), ("q8_0", 64), ("q4_k", 512), ("q6_k", 512)])
 def test_unit_vector_gives_column(fmt, K):
     N = 7
     W, _ = synth.problem(fmt, N, K, 1, seed=5)
