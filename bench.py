@@ -259,6 +259,19 @@ def measure_rows(torch, qmv, synth, dev):
     res["c5_qmv_q4_k_21504x5376"] = {"us": ms * 1e3, "bytes": b, "GB/s": b / ms / 1e6}
     del slots
 
+    # Q6_K at the FFN gate shape, and the FFN down shape (K = 21504) in Q6_K,
+    # Q4_K and Q4_0, 8 slots each
+    for name, fmt, entry in (("q6k_gate", "q6_k", qmv.qmv_q6_k), ("q6k_down", "q6_k", qmv.qmv_q6_k),
+                             ("q4k_down", "q4_k", qmv.qmv_q4_k), ("c4", "q4_0", qmv.qmv_q4_0)):
+        c = synth.CONFIGS[name]
+        W, x = synth.config_problem(name, M=1)
+        slots = [t(W) for _ in range(8)]
+        xd, y = t(x), torch.empty((1, c["N"]), device=dev)
+        ms = _time_loop(torch, lambda i: entry(slots[i % 8], xd, y, c["N"], c["K"], 1), 100)
+        b = W.nbytes + c["K"] * 4 + c["N"] * 4
+        res[f"{name}_qmv_{fmt}_{c['N']}x{c['K']}"] = {"us": ms * 1e3, "bytes": b, "GB/s": b / ms / 1e6}
+        del slots
+
     # C4: Q4_0 x Q8 activations, 5376 x 21504, M = 1, 16, 512; 8 slots
     c = synth.CONFIGS["c4"]
     N, K = c["N"], c["K"]

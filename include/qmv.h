@@ -17,7 +17,7 @@
  *   Weights and activations are only read.  Outputs and workspaces must not
  *   overlap any input.
  * Weights W.  N rows, row-major, each row K weights stored as K/32 blocks
- *   (Q4_0, Q8_0) or K/256 super-blocks (Q4_K) in the GGUF byte layout:
+ *   (Q4_0, Q8_0) or K/256 super-blocks (Q4_K, Q6_K) in the GGUF byte layout:
  *     Q4_0 (18 B / 32 weights): fp16 d, 16 bytes of codes; byte j holds
  *          element j (low nibble) and element j+16 (high nibble);
  *          w = (q - 8) * d.
@@ -25,8 +25,13 @@
  *     Q4_K (144 B / 256 weights): fp16 d, fp16 dmin, 12 bytes packing eight
  *          6-bit sub-block scales and eight 6-bit mins, 128 code bytes;
  *          w = d * scale_j * q - dmin * min_j for sub-block j.
- *   [captable section 1: 18 B Q4_0, 144 B Q4_K; roadmap K1: Q4_0 and Q8_0
- *   dequantization]
+ *     Q6_K (210 B / 256 weights): 128 bytes of low nibbles ql, 64 bytes of
+ *          high 2-bit pairs qh, 16 int8 sub-block scales, fp16 d; element
+ *          128h + 32g + l (h < 2, g < 4, l < 32) has the low (g < 2) or
+ *          high (g >= 2) nibble of ql[64h + 32(g % 2) + l] and bits 2g, 2g+1
+ *          of qh[32h + l]; w = d * scale[e / 16] * (q - 32).
+ *   [captable section 1: 18 B Q4_0, 144 B Q4_K, 210 B Q6_K; roadmap K1:
+ *   Q4_0 and Q8_0 dequantization]
  * Activations x: float32 [M][K] row-major.  Outputs y: float32 [M][N].
  * Accumulation is float32 [roadmap K2 step 1: F32 accumulation].
  * Stream.  Work is enqueued on `stream` (0 = the null stream) and runs
@@ -39,7 +44,7 @@
  *   findings F6, F13 and F17 are the defects this rules out]:
  *     QMV_ERR_NULL       a required pointer is NULL
  *     QMV_ERR_SHAPE      N, M < 1; K < 32 or K % 32 != 0 (K % 256 != 0 for
- *                        Q4_K); a size or a byte count overflows int64, or
+ *                        Q4_K, Q6_K); a size or a byte count overflows int64, or
  *                        N >= 2^31
  *     QMV_ERR_ALIGN      W or a workspace is not 16-byte aligned, or an f32
  *                        / int32 buffer is not 4-byte aligned
@@ -88,6 +93,13 @@ int qmv_q8_0(const void* W, const float* x, float* y,
 /* As qmv_q4_0 for Q4_K weights (K % 256 == 0).
  * [captable section 1: q4k_matvec, Q4_K 144 B x f32] */
 int qmv_q4_k(const void* W, const float* x, float* y,
+             int64_t N, int64_t K, int64_t M, hipStream_t stream);
+
+/* As qmv_q4_0 for Q6_K weights (K % 256 == 0).  W must be 16-byte aligned
+ * like every weight buffer; the 210-byte super-blocks inside it are read at
+ * their 2-byte alignment.
+ * [captable section 1: q6k_matvec, Q6_K 210 B planar x f32] */
+int qmv_q6_k(const void* W, const float* x, float* y,
              int64_t N, int64_t K, int64_t M, hipStream_t stream);
 
 /* Gated GELU projection pair: h[m][n] = gelu(g) * u with g = W_gate x[m],

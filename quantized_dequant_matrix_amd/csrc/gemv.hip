@@ -1,12 +1,12 @@
-// Fused-dequant matrix-vector kernels for Q4_0, Q8_0 and Q4_K weights with
-// float32 activations and float32 accumulation, and the gated GELU pair.
+// Fused-dequant matrix-vector kernels for Q4_0, Q8_0, Q4_K and Q6_K weights
+// with float32 activations and float32 accumulation, and the gated GELU pair.
 //
 // What is computed: y[n] = sum_k w[n][k] x[k] with w decoded from the block
 // formats on the fly ["Gemma 4 M4 Max kernel roadmap", K2 step 1: direct
 // Q4_0 matrix-vector with fused dequantization and F32 accumulation; step 5:
 // gated GELU FFN projection pair; "Metal kernel capability table", section 1
-// (q4_f32_matvec, q4k_matvec) and section 4 (q4k_ffn_gate_up: both matrices
-// in one dispatch)].
+// (q4_f32_matvec, q4k_matvec, q6k_matvec) and section 4 (q4k_ffn_gate_up:
+// both matrices in one dispatch)].
 //
 // The pages' Metal kernels give each SIMD group four or eight rows with
 // threadgroup staging.  On gfx950 the layout is chosen for wave64 and HBM
@@ -27,6 +27,10 @@
 //         byte-select convert per weight; the factor 16 is folded into d.
 //   Q8_0: the signed code byte is converted directly.
 //   Q4_K: w = fma(d*scale, q, -dmin*min) per weight, exact up to one rounding.
+//   Q6_K: 4 (q - 32) as a signed byte, built from the nibble and the two high
+//         bits with shifts and one mask-merge per 4 weights, then one
+//         byte-select convert per weight; each 16-weight partial sum is
+//         scaled by d*scale (exact) and the row sum by 1/4 (exact).
 // So every product carries at most the rounding of float32 arithmetic on
 // the exact weight, and the float32 sums stay within 1e-5 * sum|w x|.
 #include <utility>
@@ -132,12 +136,65 @@ __device__ __forceinline__ float q4_k_sub_dot(const uint32_t* U, const float* xk
     return s0 + s1;
 }
 
+// ---------------------------------------------------------------- Q6_K
+// Block k (0..7) of a realigned Q6_K super-block U[54]: the 32 weights
+// 32k .. 32k+31, i.e. half h = k/4, group g = k%4.  ql in dwords 0..31, qh
+// in 32..47, int8 scales in 48..51, fp16 d in U[53].  Element
+// 128h + 32g + l takes the low (g < 2) or high (g >= 2) nibble of ql byte
+// 64h + 32(g%2) + l and bits 2g, 2g+1 of qh byte 32h + l.  The byte
+//   ((nibble << 2) | (high bits << 6)) ^ 0x80
+// is 4 (q - 32) as a signed byte.  Returns 4x the block's contribution.
+template <int k>
+__device__ __forceinline__ float q6_k_block_dot(const uint32_t* U, const float* xk) {
+    constexpr int h = k >> 2;
+    constexpr int g = k & 3;
+    const float d = half_bits_to_float(U[53]);
+    float s[2][2] = {{0.f, 0.f}, {0.f, 0.f}};
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+        const uint32_t L = U[16 * h + 8 * (g & 1) + t];
+        const uint32_t H = U[32 + 8 * h + t];
+        const uint32_t nib = (g < 2) ? (L << 2) : (L >> 2);                 // nibble -> bits 2..5
+        const uint32_t hb = (g == 0) ? (H << 6) : (g == 1) ? (H << 4) : (g == 2) ? (H << 2) : H;  // -> bits 6, 7
+        const uint32_t b = ((nib & 0x3C3C3C3Cu) | (hb & 0xC0C0C0C0u)) ^ 0x80808080u;
+        float* sp = s[t >> 2];
+        sp[0] = fmaf(sbyte<0>(b), xk[4 * t + 0], sp[0]);
+        sp[1] = fmaf(sbyte<1>(b), xk[4 * t + 1], sp[1]);
+        sp[0] = fmaf(sbyte<2>(b), xk[4 * t + 2], sp[0]);
+        sp[1] = fmaf(sbyte<3>(b), xk[4 * t + 3], sp[1]);
+    }
+    // sub-blocks 8h + 2g and 8h + 2g + 1: scale bytes 2g, 2g+1 (mod 4) of
+    // dword 48 + 2h + g/2
+    const uint32_t scw = U[48 + 2 * h + (g >> 1)];
+    const float a0 = d * sbyte<(2 * g) & 3>(scw);        // exact
+    const float a1 = d * sbyte<((2 * g) & 3) + 1>(scw);  // exact
+    return fmaf(a1, s[1][0] + s[1][1], a0 * (s[0][0] + s[0][1]));
+}
+
+// Q6_K words as loaded -- U[0..51] = super-block bytes [sh, sh + 208),
+// U[52] = the 16-bit rest (bytes 208-209 if sh = 0, bytes 0-1 if sh = 2) --
+// become the super-block's own dwords 0..51 and d in U[53].  One v_perm_b32
+// per dword with a per-lane selector: bytes 4-7 of {U[i], U[i-1]} (U[i]
+// itself) when sh = 0, bytes 2-5 when sh = 2.
+__device__ __forceinline__ void q6_k_realign(uint32_t* U, uint32_t sh) {
+    const uint32_t sel = sh ? 0x05040302u : 0x07060504u;
+    U[53] = sh ? (U[51] >> 16) : U[52];
+#pragma unroll
+    for (int i = 51; i > 0; --i) U[i] = __builtin_amdgcn_perm(U[i], U[i - 1], sel);
+    U[0] = __builtin_amdgcn_perm(U[0], U[52] << 16, sel);
+}
+
 template <int F, int k>
 __device__ __forceinline__ float unit_block_dot(const uint32_t* U, const float* xk) {
     if constexpr (F == kQ4_0) return q4_0_block_dot<k>(U, xk);
     else if constexpr (F == kQ8_0) return q8_0_block_dot<k>(U, xk);
-    else return q4_k_sub_dot<k>(U, xk);
+    else if constexpr (F == kQ4_K) return q4_k_sub_dot<k>(U, xk);
+    else return q6_k_block_dot<k>(U, xk);
 }
+
+// Factor that turns a row's sum of unit_block_dot results into y.
+template <int F>
+constexpr float kRowScale = (F == kQ4_0) ? 0.0625f : (F == kQ6_K ? 0.25f : 1.0f);
 
 // Stage x[0..K) into LDS as G padded unit slices.  Each thread issues a batch
 // of loads before the matching LDS writes (indices past the end are clamped
@@ -201,7 +258,9 @@ void gemv_unit_kernel(const uint8_t* __restrict__ W0, const uint8_t* __restrict_
     const int wave_stride = gridDim.x * kWavesPerBlock;
     int pass = blockIdx.x * kWavesPerBlock + (threadIdx.x / kWave);
 
-    uint32_t U[NM * R][VEC * 4];
+    constexpr bool kQ6 = (F == kQ6_K);
+    uint32_t U[NM * R][VEC * 4 + (kQ6 ? 2 : 0)];
+    uint32_t sh[NM * R];  // Q6_K: byte offset of the super-block past its dword (0 or 2)
     auto load = [&](int p) {
 #pragma unroll
         for (int r = 0; r < R; ++r) {
@@ -212,14 +271,35 @@ void gemv_unit_kernel(const uint8_t* __restrict__ W0, const uint8_t* __restrict_
 #pragma unroll
             for (int m = 0; m < NM; ++m) {
                 const uint8_t* base = (m == 0 ? W0 : W1) + row * row_bytes + u * UB;
-                const uint4* src = reinterpret_cast<const uint4*>(base);
+                if constexpr (kQ6) {
+                    // W is 16-byte aligned and super-blocks are 210 B, so a
+                    // super-block starts 0 or 2 (= sh) bytes past a dword.
+                    // Its bytes [sh, sh + 208) are 13 dword-aligned 16-byte
+                    // pieces; the two bytes left over ([208, 210) when sh = 0,
+                    // [0, 2) when sh = 2) come in one 16-bit load.  Every
+                    // load stays inside the super-block.
+                    const uint32_t o = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(base) & 2);
+                    sh[m * R + r] = o;
+                    const u32x4_a4* src = reinterpret_cast<const u32x4_a4*>(base + o);
 #pragma unroll
-                for (int t = 0; t < VEC; ++t) {
-                    const uint4 v = src[t];
-                    U[m * R + r][4 * t + 0] = v.x;
-                    U[m * R + r][4 * t + 1] = v.y;
-                    U[m * R + r][4 * t + 2] = v.z;
-                    U[m * R + r][4 * t + 3] = v.w;
+                    for (int t = 0; t < VEC; ++t) {
+                        const u32x4_a4 v = src[t];
+                        U[m * R + r][4 * t + 0] = v.x;
+                        U[m * R + r][4 * t + 1] = v.y;
+                        U[m * R + r][4 * t + 2] = v.z;
+                        U[m * R + r][4 * t + 3] = v.w;
+                    }
+                    U[m * R + r][52] = *reinterpret_cast<const uint16_t*>(base + (o ? 0 : 208));
+                } else {
+                    const uint4* src = reinterpret_cast<const uint4*>(base);
+#pragma unroll
+                    for (int t = 0; t < VEC; ++t) {
+                        const uint4 v = src[t];
+                        U[m * R + r][4 * t + 0] = v.x;
+                        U[m * R + r][4 * t + 1] = v.y;
+                        U[m * R + r][4 * t + 2] = v.z;
+                        U[m * R + r][4 * t + 3] = v.w;
+                    }
                 }
             }
         }
@@ -240,6 +320,10 @@ void gemv_unit_kernel(const uint8_t* __restrict__ W0, const uint8_t* __restrict_
         float acc[NM * R];
 #pragma unroll
         for (int i = 0; i < NM * R; ++i) acc[i] = 0.f;
+        if constexpr (kQ6) {
+#pragma unroll
+            for (int i = 0; i < NM * R; ++i) q6_k_realign(U[i], sh[i]);
+        }
         static_for<8>([&](auto kc) {
             constexpr int k = decltype(kc)::value;
             float xk[32];
@@ -262,7 +346,7 @@ void gemv_unit_kernel(const uint8_t* __restrict__ W0, const uint8_t* __restrict_
             }
         });
         const int row0 = (pass * S + seg) * R;
-        constexpr float kScale = (F == kQ4_0) ? 0.0625f : 1.0f;
+        constexpr float kScale = kRowScale<F>;
 #pragma unroll
         for (int r = 0; r < R; ++r) {
             float v0 = segment_sum(acc[r], u, L) * kScale;
@@ -279,9 +363,10 @@ void gemv_unit_kernel(const uint8_t* __restrict__ W0, const uint8_t* __restrict_
 }
 
 // --------------------------------------------------------- generic kernel
-// Any K % 32 == 0 (K % 256 == 0 for Q4_K).  One wave per row, lanes stride
-// over the row's blocks, activations read from global memory.  Rows need
-// not be 16-byte aligned; Q4_0 / Q8_0 blocks are read with 16-bit loads.
+// Any K % 32 == 0 (K % 256 == 0 for Q4_K and Q6_K).  One wave per row, lanes
+// stride over the row's blocks, activations read from global memory.  Rows
+// need not be 16-byte aligned; Q4_0 / Q8_0 / Q6_K blocks are read with
+// 16-bit loads.
 template <int F>
 __device__ __forceinline__ float generic_block_dot(const uint8_t* __restrict__ row, int64_t b,
                                                    const float* __restrict__ x) {
@@ -313,6 +398,20 @@ __device__ __forceinline__ float generic_block_dot(const uint8_t* __restrict__ r
             s = fmaf(static_cast<float>(static_cast<int8_t>(two >> 8)), xb[2 * h + 1], s);
         }
         return d * s;
+    } else if constexpr (F == kQ6_K) {
+        // 2-byte aligned super-block: 16-bit loads
+        const uint16_t* p = reinterpret_cast<const uint16_t*>(row + 210 * b);
+        uint32_t U[54];
+#pragma unroll
+        for (int i = 0; i < 52; ++i) U[i] = static_cast<uint32_t>(p[2 * i]) | (static_cast<uint32_t>(p[2 * i + 1]) << 16);
+        U[53] = p[104];
+        const float* xb = x + 256 * b;
+        float s = 0.f;
+        static_for<8>([&](auto kc) {
+            constexpr int k = decltype(kc)::value;
+            s += q6_k_block_dot<k>(U, xb + 32 * k);
+        });
+        return 0.25f * s;
     } else {
         const uint4* src = reinterpret_cast<const uint4*>(row + 144 * b);
         uint32_t U[36];
@@ -376,8 +475,8 @@ hipError_t launch_unit(const void* W0, const void* W1, const float* x, float* y,
 template <int F, bool PAIR>
 hipError_t launch_generic(const void* W0, const void* W1, const float* x, float* y, int N, int64_t K,
                           hipStream_t stream) {
-    const int64_t per = (F == kQ4_K) ? 256 : 32;
-    const int64_t bytes = (F == kQ4_0) ? 18 : (F == kQ8_0 ? 34 : 144);
+    const int64_t per = (F == kQ4_K || F == kQ6_K) ? 256 : 32;
+    const int64_t bytes = (F == kQ4_0) ? 18 : (F == kQ8_0 ? 34 : (F == kQ4_K ? 144 : 210));
     const int64_t nb = K / per;
     const int max_blocks = device_cus() * 8;
     int blocks = (N + kWavesPerBlock - 1) / kWavesPerBlock;
@@ -422,9 +521,12 @@ hipError_t launch_gemv(int fmt, const void* W, const void* W_up, const float* x,
     case kQ8_0:
         return unit ? launch_unit<kQ8_0, 1, false>(W, nullptr, x, y, N, G, stream)
                     : launch_generic<kQ8_0, false>(W, nullptr, x, y, N, K, stream);
-    default:
+    case kQ4_K:
         return unit ? launch_unit<kQ4_K, 1, false>(W, nullptr, x, y, N, G, stream)
                     : launch_generic<kQ4_K, false>(W, nullptr, x, y, N, K, stream);
+    default:
+        return unit ? launch_unit<kQ6_K, 1, false>(W, nullptr, x, y, N, G, stream)
+                    : launch_generic<kQ6_K, false>(W, nullptr, x, y, N, K, stream);
     }
 }
 

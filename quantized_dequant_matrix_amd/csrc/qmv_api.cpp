@@ -43,8 +43,8 @@ int launched(hipError_t e) { return e == hipSuccess ? QMV_OK : QMV_ERR_LAUNCH; }
 int gemv(int fmt, const void* W, const void* W_up, const float* x, float* y, int64_t N, int64_t K, int64_t M,
          hipStream_t stream) {
     if (!W || !x || !y) return QMV_ERR_NULL;
-    const int64_t elems = (fmt == 2) ? 256 : 32;
-    const int64_t bytes = (fmt == 0) ? 18 : (fmt == 1 ? 34 : 144);
+    const int64_t elems = (fmt >= 2) ? 256 : 32;
+    const int64_t bytes = (fmt == 0) ? 18 : (fmt == 1 ? 34 : (fmt == 2 ? 144 : 210));
     int rc = check_shape(N, K, M, elems, bytes);
     if (rc) return rc;
     if (!aligned(W, 16) || (W_up && !aligned(W_up, 16)) || !aligned(x, 4) || !aligned(y, 4)) return QMV_ERR_ALIGN;
@@ -63,7 +63,7 @@ const char* qmv_status_str(int status) {
     switch (status) {
     case QMV_OK: return "ok";
     case QMV_ERR_NULL: return "null pointer";
-    case QMV_ERR_SHAPE: return "invalid shape (N, M >= 1; K >= 32, K % 32 == 0, K % 256 == 0 for Q4_K; no overflow)";
+    case QMV_ERR_SHAPE: return "invalid shape (N, M >= 1; K >= 32, K % 32 == 0, K % 256 == 0 for Q4_K and Q6_K; no overflow)";
     case QMV_ERR_ALIGN: return "misaligned buffer (W and workspace 16 B, float/int32 buffers 4 B)";
     case QMV_ERR_WORKSPACE: return "workspace too small";
     case QMV_ERR_LAUNCH: return "kernel launch failed";
@@ -82,6 +82,10 @@ int qmv_q8_0(const void* W, const float* x, float* y, int64_t N, int64_t K, int6
 
 int qmv_q4_k(const void* W, const float* x, float* y, int64_t N, int64_t K, int64_t M, hipStream_t stream) {
     return gemv(2, W, nullptr, x, y, N, K, M, stream);
+}
+
+int qmv_q6_k(const void* W, const float* x, float* y, int64_t N, int64_t K, int64_t M, hipStream_t stream) {
+    return gemv(3, W, nullptr, x, y, N, K, M, stream);
 }
 
 int qmv_q4_0_geglu(const void* W_gate, const void* W_up, const float* x, float* h, int64_t N, int64_t K,

@@ -12,7 +12,8 @@ constexpr int kWavesPerBlock = kBlockThreads / kWave;
 
 // A "unit" is the smallest run of whole blocks that starts and ends on a
 // 16-byte boundary: 8 Q4_0 blocks (144 B), 8 Q8_0 blocks (272 B) or one Q4_K
-// super-block (144 B).  Each covers 256 weights.  With K % 256 == 0 every row,
+// super-block (144 B); and, as the one exception, one Q6_K super-block
+// (210 B, 2-byte aligned).  Each covers 256 weights.  With K % 256 == 0 every row,
 // and every unit in it, is 16-byte aligned, so a lane can stream a unit with
 // plain 16-byte loads and find each block at a compile-time byte offset.
 constexpr int kUnitElems = 256;
@@ -20,12 +21,20 @@ constexpr int kUnitElems = 256;
 // so that lanes holding consecutive units start on different LDS banks.
 constexpr int kXsStride = kUnitElems + 4;
 
-enum Format : int { kQ4_0 = 0, kQ8_0 = 1, kQ4_K = 2 };
+enum Format : int { kQ4_0 = 0, kQ8_0 = 1, kQ4_K = 2, kQ6_K = 3 };
 
 template <int F> struct UnitInfo;
 template <> struct UnitInfo<kQ4_0> { static constexpr int kBytes = 144; static constexpr int kVec = 9; };
 template <> struct UnitInfo<kQ8_0> { static constexpr int kBytes = 272; static constexpr int kVec = 17; };
 template <> struct UnitInfo<kQ4_K> { static constexpr int kBytes = 144; static constexpr int kVec = 9; };
+// A Q6_K super-block (210 B) starts on a 2-byte boundary only: its lane reads
+// the 13 dword-aligned 16-byte pieces from the dword at or before its start
+// and two 16-bit words at its end, then realigns (see gemv.hip).
+template <> struct UnitInfo<kQ6_K> { static constexpr int kBytes = 210; static constexpr int kVec = 13; };
+
+// 16-byte vector with 4-byte alignment: one global_load_dwordx4 from an
+// address that is only dword aligned.
+typedef uint32_t u32x4_a4 __attribute__((ext_vector_type(4), aligned(4)));
 
 __device__ __forceinline__ float half_bits_to_float(uint32_t bits) {
     return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(bits)));

@@ -13,7 +13,7 @@ namespace qmv {
 int device_cus();
 
 // One matrix-vector product (one activation row).  fmt: 0 Q4_0, 1 Q8_0,
-// 2 Q4_K.  W_up != nullptr selects the gated pair (Q4_0 only):
+// 2 Q4_K, 3 Q6_K.  W_up != nullptr selects the gated pair (Q4_0 only):
 // y = gelu(W x) * (W_up x).
 hipError_t launch_gemv(int fmt, const void* W, const void* W_up, const float* x, float* y,
                        int64_t N, int64_t K, hipStream_t stream);

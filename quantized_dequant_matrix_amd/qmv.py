@@ -30,6 +30,7 @@ _SIGS = {
     "qmv_q4_0": ([_P, _P, _P, _I64, _I64, _I64, _P], ctypes.c_int),
     "qmv_q8_0": ([_P, _P, _P, _I64, _I64, _I64, _P], ctypes.c_int),
     "qmv_q4_k": ([_P, _P, _P, _I64, _I64, _I64, _P], ctypes.c_int),
+    "qmv_q6_k": ([_P, _P, _P, _I64, _I64, _I64, _P], ctypes.c_int),
     "qmv_q4_0_geglu": ([_P, _P, _P, _P, _I64, _I64, _I64, _P], ctypes.c_int),
     "qmm_q4_0_q8act_ws_bytes": ([_I64, _I64, _I64], _SZ),
     "qmm_q4_0_q8act": ([_P, _P, _P, _I64, _I64, _I64, _P, _SZ, _P], ctypes.c_int),
@@ -95,6 +96,10 @@ def qmv_q8_0(W, x, y, N, K, M=1, stream=None):
 
 def qmv_q4_k(W, x, y, N, K, M=1, stream=None):
     _call("qmv_q4_k", _ptr(W), _ptr(x), _ptr(y), N, K, M, _stream(stream))
+
+
+def qmv_q6_k(W, x, y, N, K, M=1, stream=None):
+    _call("qmv_q6_k", _ptr(W), _ptr(x), _ptr(y), N, K, M, _stream(stream))
 
 
 def qmv_q4_0_geglu(W_gate, W_up, x, h, N, K, M=1, stream=None):

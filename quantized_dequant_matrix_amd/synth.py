@@ -45,7 +45,8 @@ BLOCK_ELEMS = {"q4_0": 32, "q8_0": 32, "q4_k": 256, "q6_k": 256}
 
 # Seeds of the five workloads; the up-projection matrix of the gated pair
 # uses its own seed.
-SEEDS = {"c1": 101, "c2": 102, "c2_up": 1102, "c3": 103, "c4": 104, "c5": 105}
+SEEDS = {"c1": 101, "c2": 102, "c2_up": 1102, "c3": 103, "c4": 104, "c5": 105,
+         "q6k_gate": 106, "q6k_down": 107, "qkv": 108, "q4k_down": 109}
 
 
 def row_bytes(fmt: str, K: int) -> int:
@@ -219,6 +220,11 @@ CONFIGS = {
     "c3": dict(fmt="q8_0", N=262144, K=5376, M=1, k=10, softcap=30.0),
     "c4": dict(fmt="q4_0", N=5376, K=21504, Ms=(1, 16, 512)),
     "c5": dict(fmt="q4_k", N=21504, K=5376, M=1),
+    # Q6_K at the FFN gate shape (the unit kernel's shape, next to c5) and at
+    # the FFN down shape 5376 x 21504, where Q4_K_M files keep Q6_K
+    "q6k_gate": dict(fmt="q6_k", N=21504, K=5376, M=1),
+    "q6k_down": dict(fmt="q6_k", N=5376, K=21504, M=1),
+    "q4k_down": dict(fmt="q4_k", N=5376, K=21504, M=1),
 }
 
 

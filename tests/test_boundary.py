@@ -26,7 +26,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported_and_bound():
     names = declared_functions()
-    assert "qmv_q4_0" in names and "logits_topk" in names and len(names) == 16
+    assert "qmv_q4_0" in names and "logits_topk" in names and len(names) == 17
     for n in names:
         assert hasattr(qmv.lib, n), n
     assert sorted(qmv.EXPORTS) == names
@@ -59,7 +59,7 @@ def call(name, *args):
     return getattr(qmv.lib, name)(*args)
 
 
-@pytest.mark.parametrize("name", ["qmv_q4_0", "qmv_q8_0", "qmv_q4_k"])
+@pytest.mark.parametrize("name", ["qmv_q4_0", "qmv_q8_0", "qmv_q4_k", "qmv_q6_k"])
 def test_gemv_validation(name):
     assert call(name, None, FAKE, FAKE, 8, 256, 1, S) == NUL
     assert call(name, FAKE, None, FAKE, 8, 256, 1, S) == NUL
@@ -76,8 +76,10 @@ def test_gemv_validation(name):
     assert call(name, FAKE, FAKE, FAKE + 1, 8, 256, 1, S) == ALIGN
 
 
-def test_q4_k_needs_whole_superblocks():
-    assert call("qmv_q4_k", FAKE, FAKE, FAKE, 8, 288, 1, S) == SHAPE
+@pytest.mark.parametrize("name", ["qmv_q4_k", "qmv_q6_k"])
+def test_k_quants_need_whole_superblocks(name):
+    assert call(name, FAKE, FAKE, FAKE, 8, 288, 1, S) == SHAPE
+    assert call(name, FAKE, FAKE, FAKE, 8, 256 * 84 + 32, 1, S) == SHAPE
 
 
 def test_geglu_validation():

@@ -1,4 +1,4 @@
-"""Parity of the HIP matrix-vector kernels (Q4_0, Q8_0, Q4_K, gated pair)
+"""Parity of the HIP matrix-vector kernels (Q4_0, Q8_0, Q4_K, Q6_K, gated pair)
 with the float64 oracle, element by element, through the C ABI.
 
 Bar: |y - y_ref| <= 1e-5 * sum_i |w_i x_i| + 1e-6 for every output; the
@@ -13,7 +13,7 @@ from gpu_util import assert_within, dev, empty, host, say
 
 pytestmark = pytest.mark.gpu
 
-FMTS = ["q4_0", "q8_0", "q4_k"]
+FMTS = ["q4_0", "q8_0", "q4_k", "q6_k"]
 
 
 def _qmv():
@@ -37,8 +37,8 @@ SHAPES = [(1, 256), (5, 512), (64, 256), (65, 256), (3, 768), (100, 1024), (33, 
 @pytest.mark.parametrize("fmt", FMTS)
 @pytest.mark.parametrize("N,K", SHAPES)
 def test_shapes(fmt, N, K):
-    if fmt == "q4_k" and K % 256:
-        pytest.skip("Q4_K needs K % 256 == 0")
+    if fmt in ("q4_k", "q6_k") and K % 256:
+        pytest.skip("Q4_K and Q6_K need K % 256 == 0")
     seed = 7 * N + K
     say(f"qmv_{fmt} N={N} K={K} seed={seed}")
     W, x = synth.problem(fmt, N, K, 1, seed)
@@ -57,7 +57,7 @@ def test_batched_rows(fmt):
     assert_within(y, yr, oracle.float_tol(S), f"qmv_{fmt} M={M}")
 
 
-@pytest.mark.parametrize("name,fmt", [("c1", "q4_0"), ("c2", "q4_0"), ("c5", "q4_k")])
+@pytest.mark.parametrize("name,fmt", [("c1", "q4_0"), ("c2", "q4_0"), ("c5", "q4_k"), ("q6k_gate", "q6_k")])
 def test_workloads_full(name, fmt):
     c = synth.CONFIGS[name]
     say(f"qmv_{fmt} workload {name} N={c['N']} K={c['K']}")
@@ -79,7 +79,8 @@ def test_logit_workload_rows_sampled():
     assert_within(y[:, rows], yr, oracle.float_tol(S), "c3 rows")
 
 
-@pytest.mark.parametrize("fmt,K", [("q4_0", 512), ("q8_0", 512), ("q4_k", 512), ("q4_0", 96), ("q8_0", 160)])
+@pytest.mark.parametrize("fmt,K", [("q4_0", 512), ("q8_0", 512), ("q4_k", 512), ("q6_k", 512), ("q6_k", 768),
+                                   ("q4_0", 96), ("q8_0", 160)])
 def test_unit_vectors_give_columns(fmt, K):
     N = 70
     say(f"qmv_{fmt} unit vectors K={K}")
@@ -92,10 +93,28 @@ def test_unit_vectors_give_columns(fmt, K):
     y = run_gemv(fmt, W, E, N, K, len(cols))
     dq = np.stack([oracle.dequant_row(fmt, W[n * rb:(n + 1) * rb], K) for n in range(N)])
     ref = dq[:, cols].T
-    if fmt == "q4_k":
-        # d*scale*q - dmin*min is exact in float64 and rounded once to float32
+    if fmt in ("q4_k", "q6_k"):
+        # d*scale*q - dmin*min, and d*scale*(q - 32) (up to 25 significant
+        # bits), are exact in float64 and rounded once to float32
         ref = ref.astype(np.float32)
     assert np.array_equal(y, ref)
+
+
+def test_q6_k_extreme_codes_and_scales():
+    # q in {0, 63} and scales in {-128, 127}: the largest products the
+    # signed-byte decode forms; rows alternate the super-block alignment
+    N, K = 37, 2304
+    say("qmv_q6_k extreme codes and scales")
+    rng = np.random.default_rng(21)
+    nb = N * K // 256
+    q = rng.choice(np.array([0, 63, 32, 31, 33], np.uint8), size=(nb, 256))
+    sc = rng.choice(np.array([-128, 127, -1, 0], np.int8), size=(nb, 16))
+    d = (np.abs(rng.standard_normal(nb)) * 1e-4).astype(np.float16)
+    W = synth.pack_q6_k(d, sc, q)
+    x = rng.standard_normal((1, K)).astype(np.float32)
+    y = run_gemv("q6_k", W, x, N, K)
+    yr, S = oracle.qmv("q6_k", W, N, K, x)
+    assert_within(y, yr, oracle.float_tol(S), "q6_k extremes")
 
 
 def test_zero_weights_exactly_zero():
