@@ -270,6 +270,14 @@ def measure_rows(torch, qmv, synth, dev):
         ms = _time_loop(torch, lambda i: entry(slots[i % 8], xd, y, c["N"], c["K"], 1), 100)
         b = W.nbytes + c["K"] * 4 + c["N"] * 4
         res[f"{name}_qmv_{fmt}_{c['N']}x{c['K']}"] = {"us": ms * 1e3, "bytes": b, "GB/s": b / ms / 1e6}
+        if name.endswith("down"):
+            # the same product with the GELU gate folded into its input (reads g and u)
+            ud = t(synth.activations(1, c["K"], synth.SEEDS[name] + 1))
+            gated = getattr(qmv, f"qmv_{fmt}_geglu_down")
+            ms = _time_loop(torch, lambda i: gated(slots[i % 8], xd, ud, y, c["N"], c["K"], 1), 100)
+            b = W.nbytes + 2 * c["K"] * 4 + c["N"] * 4
+            res[f"{name}_qmv_{fmt}_geglu_down_{c['N']}x{c['K']}"] = {"us": ms * 1e3, "bytes": b,
+                                                                   "GB/s": b / ms / 1e6}
         del slots
 
     # C4: Q4_0 x Q8 activations, 5376 x 21504, M = 1, 16, 512; 8 slots

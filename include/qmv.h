@@ -112,6 +112,24 @@ int qmv_q6_k(const void* W, const float* x, float* y,
 int qmv_q4_0_geglu(const void* W_gate, const void* W_up, const float* x, float* h,
                    int64_t N, int64_t K, int64_t M, hipStream_t stream);
 
+/* Down projection of a gated FFN with the GELU gate folded into its input:
+ *   y[m][n] = sum_k w[n][k] * h[m][k],  h[m][k] = gelu(g[m][k]) * u[m][k],
+ * gelu the tanh form above, h formed in float32 while the activations are
+ * staged (never written to memory).  g and u: float32 [M][K], the gate and
+ * up projections' outputs; W_down: [N][K] in the format of the name
+ * (K % 256 == 0 for Q4_K and Q6_K).  Long rows (K > 16128, e.g. the
+ * 21504-wide FFN down projection) split K across the waves of a workgroup
+ * and add the slices in a fixed order.
+ * [captable section 4: q4k_geglu_gelu_tanh_down, q6k_geglu_gelu_tanh_down
+ *  (GELU-tanh product fused into the down projection); roadmap K2 step 5:
+ *  gated GELU FFN] */
+int qmv_q4_0_geglu_down(const void* W_down, const float* g, const float* u, float* y,
+                        int64_t N, int64_t K, int64_t M, hipStream_t stream);
+int qmv_q4_k_geglu_down(const void* W_down, const float* g, const float* u, float* y,
+                        int64_t N, int64_t K, int64_t M, hipStream_t stream);
+int qmv_q6_k_geglu_down(const void* W_down, const float* g, const float* u, float* y,
+                        int64_t N, int64_t K, int64_t M, hipStream_t stream);
+
 /* Q4_0 weights times Q8-quantized activations, y float32 [M][N].
  * Step 1 quantizes each 32-element block of x (float32 arithmetic):
  *   amax = max|x|, d_x = amax / 127 (IEEE division),

@@ -196,53 +196,154 @@ __device__ __forceinline__ float unit_block_dot(const uint32_t* U, const float* 
 template <int F>
 constexpr float kRowScale = (F == kQ4_0) ? 0.0625f : (F == kQ6_K ? 0.25f : 1.0f);
 
-// Stage x[0..K) into LDS as G padded unit slices.  Each thread issues a batch
-// of loads before the matching LDS writes (indices past the end are clamped
-// to the last element, which is then written twice with the same value), so a
-// workgroup waits for a couple of memory round trips, not one per element.
+// Stage the activations into LDS as G padded unit slices: x[0..K), or, for
+// the down projection of a gated FFN (GIN), gelu(x[k]) * xu[k] formed here
+// in float32.  Each thread issues a batch of loads before the matching LDS
+// writes (indices past the end are clamped to the last element, which is
+// then written twice with the same value), so a workgroup waits for a couple
+// of memory round trips, not one per element.
 constexpr int kMaxUnits = 63;
-__device__ __forceinline__ void stage_x(float* xs, const float* __restrict__ x, int G) {
-    if ((reinterpret_cast<uintptr_t>(x) & 15) == 0) {
-        constexpr int kPer = 4;  // 16-byte loads in flight per thread
+
+template <bool GIN>
+__device__ __forceinline__ float staged_value(float a, float b) {
+    if constexpr (GIN) return gelu_tanh(a) * b;
+    else return a;
+}
+
+// NT: the workgroup's thread count (every thread of the workgroup calls this).
+template <bool GIN>
+__device__ __forceinline__ void stage_x(float* xs, const float* __restrict__ x, const float* __restrict__ xu, int G,
+                                        const int NT) {
+    const bool vec = ((reinterpret_cast<uintptr_t>(x) | (GIN ? reinterpret_cast<uintptr_t>(xu) : 0)) & 15) == 0;
+    if (vec) {
+        constexpr int kPer = GIN ? 2 : 4;  // 16-byte loads in flight per thread (per input)
         const int n4 = G * (kUnitElems / 4);
-        for (int base = 0; base < n4; base += kPer * kBlockThreads) {
-            float4 v[kPer];
+        for (int base = 0; base < n4; base += kPer * NT) {
+            float4 v[kPer], w[GIN ? kPer : 1];
 #pragma unroll
             for (int j = 0; j < kPer; ++j) {
-                const int i = min(base + j * kBlockThreads + static_cast<int>(threadIdx.x), n4 - 1);
+                const int i = min(base + j * NT + static_cast<int>(threadIdx.x), n4 - 1);
                 v[j] = reinterpret_cast<const float4*>(x)[i];
+                if constexpr (GIN) w[j] = reinterpret_cast<const float4*>(xu)[i];
             }
 #pragma unroll
             for (int j = 0; j < kPer; ++j) {
-                const int i = min(base + j * kBlockThreads + static_cast<int>(threadIdx.x), n4 - 1);
+                const int i = min(base + j * NT + static_cast<int>(threadIdx.x), n4 - 1);
+                if constexpr (GIN) {
+                    v[j].x = staged_value<true>(v[j].x, w[j].x);
+                    v[j].y = staged_value<true>(v[j].y, w[j].y);
+                    v[j].z = staged_value<true>(v[j].z, w[j].z);
+                    v[j].w = staged_value<true>(v[j].w, w[j].w);
+                }
                 *reinterpret_cast<float4*>(xs + (i >> 6) * kXsStride + (i & 63) * 4) = v[j];
             }
         }
     } else {
-        // unaligned x: 4 scalar loads in flight per thread (few registers:
-        // the weights of the first pass are already in flight)
+        // unaligned activations: 4 scalar loads in flight per thread and
+        // input (few registers: the weights of the first pass are already
+        // in flight)
         const int n = G * kUnitElems;
-        for (int base = 0; base < n; base += 4 * kBlockThreads) {
-            float v[4];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) v[j] = x[min(base + j * kBlockThreads + static_cast<int>(threadIdx.x), n - 1)];
+        for (int base = 0; base < n; base += 4 * NT) {
+            float v[4], w[4];
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const int i = min(base + j * kBlockThreads + static_cast<int>(threadIdx.x), n - 1);
-                xs[(i >> 8) * kXsStride + (i & 255)] = v[j];
+                const int i = min(base + j * NT + static_cast<int>(threadIdx.x), n - 1);
+                v[j] = x[i];
+                w[j] = GIN ? xu[i] : 0.f;
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int i = min(base + j * NT + static_cast<int>(threadIdx.x), n - 1);
+                xs[(i >> 8) * kXsStride + (i & 255)] = staged_value<GIN>(v[j], w[j]);
             }
         }
     }
+}
+
+// One lane's 256-weight unit at base: UnitInfo<F>::kVec 16-byte loads into
+// U (and, for Q6_K, the 16-bit rest into U[52] and the super-block's offset
+// past its dword into sh; q6_k_realign then puts the words in place).
+template <int F>
+__device__ __forceinline__ void load_unit(uint32_t* U, uint32_t& sh, const uint8_t* base) {
+    constexpr int VEC = UnitInfo<F>::kVec;
+    if constexpr (F == kQ6_K) {
+        // W is 16-byte aligned and super-blocks are 210 B, so a super-block
+        // starts 0 or 2 (= sh) bytes past a dword.  Its bytes [sh, sh + 208)
+        // are 13 dword-aligned 16-byte pieces; the two bytes left over
+        // ([208, 210) when sh = 0, [0, 2) when sh = 2) come in one 16-bit
+        // load.  Every load stays inside the super-block.
+        const uint32_t o = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(base) & 2);
+        sh = o;
+        const u32x4_a4* src = reinterpret_cast<const u32x4_a4*>(base + o);
+#pragma unroll
+        for (int t = 0; t < VEC; ++t) {
+            const u32x4_a4 v = src[t];
+            U[4 * t + 0] = v.x;
+            U[4 * t + 1] = v.y;
+            U[4 * t + 2] = v.z;
+            U[4 * t + 3] = v.w;
+        }
+        U[52] = *reinterpret_cast<const uint16_t*>(base + (o ? 0 : 208));
+    } else {
+        sh = 0;
+        const uint4* src = reinterpret_cast<const uint4*>(base);
+#pragma unroll
+        for (int t = 0; t < VEC; ++t) {
+            const uint4 v = src[t];
+            U[4 * t + 0] = v.x;
+            U[4 * t + 1] = v.y;
+            U[4 * t + 2] = v.z;
+            U[4 * t + 3] = v.w;
+        }
+    }
+}
+
+template <int F>
+constexpr int kUnitWords = UnitInfo<F>::kVec * 4 + (F == kQ6_K ? 2 : 0);
+
+// acc[i] = the sum over unit i's 256 weights of (decoded weight) * x, for NR
+// units held in U that share the activation slice xw (LDS), times the
+// format's 1/kRowScale.
+template <int F, int NR>
+__device__ __forceinline__ void dot_units(uint32_t (&U)[NR][kUnitWords<F>], const uint32_t (&sh)[NR],
+                                          const float* xw, float (&acc)[NR]) {
+#pragma unroll
+    for (int i = 0; i < NR; ++i) acc[i] = 0.f;
+    if constexpr (F == kQ6_K) {
+#pragma unroll
+        for (int i = 0; i < NR; ++i) q6_k_realign(U[i], sh[i]);
+    }
+    static_for<8>([&](auto kc) {
+        constexpr int k = decltype(kc)::value;
+        float xk[32];
+        const float4* xv = reinterpret_cast<const float4*>(xw + 32 * k);
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+            const float4 v = xv[t];
+            xk[4 * t + 0] = v.x;
+            xk[4 * t + 1] = v.y;
+            xk[4 * t + 2] = v.z;
+            xk[4 * t + 3] = v.w;
+        }
+#pragma unroll
+        for (int i = 0; i < NR; ++i) {
+            acc[i] += unit_block_dot<F, k>(U[i], xk);
+            // Materialize the sum here: otherwise the compiler sinks the
+            // work of later units past earlier reductions and keeps every
+            // block's activations live in registers.
+            asm volatile("" : "+v"(acc[i]));
+        }
+    });
 }
 
 // ------------------------------------------------------------ unit kernel
 // K % 256 == 0 and G = K/256 <= 63.  Lane (segment s, unit u) of a wave
 // handles unit u of R consecutive rows per pass; a pass covers S*R rows.
 // PAIR: the same rows of two matrices (gate, up), output gelu(g) * u.
-template <int F, int R, bool PAIR>
+template <int F, int R, bool PAIR, bool GIN>
 __global__ __launch_bounds__(kBlockThreads)
 void gemv_unit_kernel(const uint8_t* __restrict__ W0, const uint8_t* __restrict__ W1,
-                      const float* __restrict__ x, float* __restrict__ y,
+                      const float* __restrict__ x, const float* __restrict__ xu, float* __restrict__ y,
                       int N, int G, int S, int npasses) {
     constexpr int VEC = UnitInfo<F>::kVec;
     constexpr int UB = UnitInfo<F>::kBytes;
@@ -258,8 +359,7 @@ void gemv_unit_kernel(const uint8_t* __restrict__ W0, const uint8_t* __restrict_
     const int wave_stride = gridDim.x * kWavesPerBlock;
     int pass = blockIdx.x * kWavesPerBlock + (threadIdx.x / kWave);
 
-    constexpr bool kQ6 = (F == kQ6_K);
-    uint32_t U[NM * R][VEC * 4 + (kQ6 ? 2 : 0)];
+    uint32_t U[NM * R][kUnitWords<F>];
     uint32_t sh[NM * R];  // Q6_K: byte offset of the super-block past its dword (0 or 2)
     auto load = [&](int p) {
 #pragma unroll
@@ -269,45 +369,14 @@ void gemv_unit_kernel(const uint8_t* __restrict__ W0, const uint8_t* __restrict_
             int row = (p * S + seg) * R + r;
             row = row < N ? row : N - 1;
 #pragma unroll
-            for (int m = 0; m < NM; ++m) {
-                const uint8_t* base = (m == 0 ? W0 : W1) + row * row_bytes + u * UB;
-                if constexpr (kQ6) {
-                    // W is 16-byte aligned and super-blocks are 210 B, so a
-                    // super-block starts 0 or 2 (= sh) bytes past a dword.
-                    // Its bytes [sh, sh + 208) are 13 dword-aligned 16-byte
-                    // pieces; the two bytes left over ([208, 210) when sh = 0,
-                    // [0, 2) when sh = 2) come in one 16-bit load.  Every
-                    // load stays inside the super-block.
-                    const uint32_t o = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(base) & 2);
-                    sh[m * R + r] = o;
-                    const u32x4_a4* src = reinterpret_cast<const u32x4_a4*>(base + o);
-#pragma unroll
-                    for (int t = 0; t < VEC; ++t) {
-                        const u32x4_a4 v = src[t];
-                        U[m * R + r][4 * t + 0] = v.x;
-                        U[m * R + r][4 * t + 1] = v.y;
-                        U[m * R + r][4 * t + 2] = v.z;
-                        U[m * R + r][4 * t + 3] = v.w;
-                    }
-                    U[m * R + r][52] = *reinterpret_cast<const uint16_t*>(base + (o ? 0 : 208));
-                } else {
-                    const uint4* src = reinterpret_cast<const uint4*>(base);
-#pragma unroll
-                    for (int t = 0; t < VEC; ++t) {
-                        const uint4 v = src[t];
-                        U[m * R + r][4 * t + 0] = v.x;
-                        U[m * R + r][4 * t + 1] = v.y;
-                        U[m * R + r][4 * t + 2] = v.z;
-                        U[m * R + r][4 * t + 3] = v.w;
-                    }
-                }
-            }
+            for (int m = 0; m < NM; ++m)
+                load_unit<F>(U[m * R + r], sh[m * R + r], (m == 0 ? W0 : W1) + row * row_bytes + u * UB);
         }
     };
 
     // Start the weight stream before staging the activations.
     if (pass < npasses) load(pass);
-    stage_x(xs, x, G);
+    stage_x<GIN>(xs, x, xu, G, kBlockThreads);
     __syncthreads();
 
     while (pass < npasses) {
@@ -318,33 +387,7 @@ void gemv_unit_kernel(const uint8_t* __restrict__ W0, const uint8_t* __restrict_
         asm volatile("" : "+v"(xoff));
         const float* xw = xs + xoff;
         float acc[NM * R];
-#pragma unroll
-        for (int i = 0; i < NM * R; ++i) acc[i] = 0.f;
-        if constexpr (kQ6) {
-#pragma unroll
-            for (int i = 0; i < NM * R; ++i) q6_k_realign(U[i], sh[i]);
-        }
-        static_for<8>([&](auto kc) {
-            constexpr int k = decltype(kc)::value;
-            float xk[32];
-            const float4* xv = reinterpret_cast<const float4*>(xw + 32 * k);
-#pragma unroll
-            for (int t = 0; t < 8; ++t) {
-                const float4 v = xv[t];
-                xk[4 * t + 0] = v.x;
-                xk[4 * t + 1] = v.y;
-                xk[4 * t + 2] = v.z;
-                xk[4 * t + 3] = v.w;
-            }
-#pragma unroll
-            for (int i = 0; i < NM * R; ++i) {
-                acc[i] += unit_block_dot<F, k>(U[i], xk);
-                // Materialize the sum here: otherwise the compiler sinks the
-                // work of later rows past earlier reductions and keeps every
-                // block's activations live in registers.
-                asm volatile("" : "+v"(acc[i]));
-            }
-        });
+        dot_units<F, NM * R>(U, sh, xw, acc);
         const int row0 = (pass * S + seg) * R;
         constexpr float kScale = kRowScale<F>;
 #pragma unroll
@@ -362,18 +405,92 @@ void gemv_unit_kernel(const uint8_t* __restrict__ W0, const uint8_t* __restrict_
     }
 }
 
+// ----------------------------------------------------------- split kernel
+// K % 256 == 0 and G = K/256 > 63: rows longer than a wave has lanes for one
+// unit each (the FFN down projection, K = 21504, has G = 84).  A workgroup
+// of RG x KS waves stages all of x once (up to 160 KB of LDS); wave (rg, kq)
+// takes K-slice kq -- units [kq*Gs, kq*Gs + Gs) -- of S rows, one unit per
+// lane as in the unit kernel.  The KS slice sums of a row meet in LDS and
+// are added in slice order, so the result does not depend on timing.
+constexpr int kSplitThreads = 1024;
+
+template <int F, bool GIN>
+__global__ __launch_bounds__(kSplitThreads)
+void gemv_split_kernel(const uint8_t* __restrict__ W, const float* __restrict__ x, const float* __restrict__ xu,
+                       float* __restrict__ y, int N, int G, int KS, int Gs, int S, int RG, int npasses) {
+    constexpr int UB = UnitInfo<F>::kBytes;
+    extern __shared__ float xs[];
+    float* red = xs + G * kXsStride;  // [2][RG][S][KS] slice sums, double-buffered by pass
+
+    const int wave = threadIdx.x / kWave;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int rg = wave / KS;
+    const int kq = wave - rg * KS;
+    const int seg = lane / Gs;
+    const int uu = lane - seg * Gs;
+    const int u = kq * Gs + uu;
+    const bool live = seg < S && u < G;
+    const int uc = u < G ? u : G - 1;  // lanes past the last unit load a valid one, summed as 0
+    const int64_t row_bytes = static_cast<int64_t>(G) * UB;
+
+    uint32_t U[1][kUnitWords<F>];
+    uint32_t sh[1];
+    auto load = [&](int p) {
+        int row = (p * RG + rg) * S + seg;
+        row = row < N ? row : N - 1;
+        load_unit<F>(U[0], sh[0], W + row * row_bytes + uc * UB);
+    };
+
+    int pass = blockIdx.x;
+    if (pass < npasses) load(pass);
+    stage_x<GIN>(xs, x, xu, G, RG * KS * kWave);  // the launch's block size
+    __syncthreads();
+
+    int buf = 0;
+    while (pass < npasses) {
+        int xoff = uc * kXsStride;
+        asm volatile("" : "+v"(xoff));
+        float acc[1];
+        dot_units<F, 1>(U, sh, xs + xoff, acc);
+        const float v = segment_sum(live ? acc[0] : 0.f, uu, Gs);
+        if (seg < S && uu == 0) red[((buf * RG + rg) * S + seg) * KS + kq] = v;
+        __syncthreads();
+        if (static_cast<int>(threadIdx.x) < RG * S) {
+            const int r = threadIdx.x;
+            const int row = pass * RG * S + r;
+            const float* part = red + (buf * RG * S + r) * KS;
+            float t = part[0];
+            for (int q = 1; q < KS; ++q) t += part[q];
+            if (row < N) y[row] = t * kRowScale<F>;
+        }
+        // The next pass writes the other buffer; this one is rewritten only
+        // after the next pass's barrier, which every reader above passes
+        // after its reads.
+        buf ^= 1;
+        pass += gridDim.x;
+        if (pass < npasses) load(pass);
+    }
+}
+
 // --------------------------------------------------------- generic kernel
-// Any K % 32 == 0 (K % 256 == 0 for Q4_K and Q6_K).  One wave per row, lanes
-// stride over the row's blocks, activations read from global memory.  Rows
-// need not be 16-byte aligned; Q4_0 / Q8_0 / Q6_K blocks are read with
-// 16-bit loads.
-template <int F>
-__device__ __forceinline__ float generic_block_dot(const uint8_t* __restrict__ row, int64_t b,
-                                                   const float* __restrict__ x) {
+// Activations of the generic kernel: x[i], or gelu(x[i]) * xu[i] for the
+// gated down projection (formed per use, float32).
+template <bool GIN>
+struct ActIn {
+    const float* __restrict__ x;
+    const float* __restrict__ xu;
+    __device__ __forceinline__ float operator()(int64_t i) const {
+        if constexpr (GIN) return gelu_tanh(x[i]) * xu[i];
+        else return x[i];
+    }
+};
+
+template <int F, bool GIN>
+__device__ __forceinline__ float generic_block_dot(const uint8_t* __restrict__ row, int64_t b, ActIn<GIN> xa) {
     if constexpr (F == kQ4_0) {
         const uint16_t* p = reinterpret_cast<const uint16_t*>(row + 18 * b);
         const float d = half_bits_to_float(p[0]);
-        const float* xb = x + 32 * b;
+        const int64_t xb = 32 * b;
         float s = 0.f;
 #pragma unroll
         for (int h = 0; h < 8; ++h) {
@@ -381,67 +498,72 @@ __device__ __forceinline__ float generic_block_dot(const uint8_t* __restrict__ r
 #pragma unroll
             for (int i = 0; i < 2; ++i) {
                 const int byte = (two >> (8 * i)) & 0xff;
-                s = fmaf(static_cast<float>((byte & 15) - 8), xb[2 * h + i], s);
-                s = fmaf(static_cast<float>((byte >> 4) - 8), xb[16 + 2 * h + i], s);
+                s = fmaf(static_cast<float>((byte & 15) - 8), xa(xb + 2 * h + i), s);
+                s = fmaf(static_cast<float>((byte >> 4) - 8), xa(xb + 16 + 2 * h + i), s);
             }
         }
         return d * s;
     } else if constexpr (F == kQ8_0) {
         const uint16_t* p = reinterpret_cast<const uint16_t*>(row + 34 * b);
         const float d = half_bits_to_float(p[0]);
-        const float* xb = x + 32 * b;
+        const int64_t xb = 32 * b;
         float s = 0.f;
 #pragma unroll
         for (int h = 0; h < 16; ++h) {
             const uint32_t two = p[1 + h];
-            s = fmaf(static_cast<float>(static_cast<int8_t>(two & 0xff)), xb[2 * h], s);
-            s = fmaf(static_cast<float>(static_cast<int8_t>(two >> 8)), xb[2 * h + 1], s);
+            s = fmaf(static_cast<float>(static_cast<int8_t>(two & 0xff)), xa(xb + 2 * h), s);
+            s = fmaf(static_cast<float>(static_cast<int8_t>(two >> 8)), xa(xb + 2 * h + 1), s);
         }
         return d * s;
-    } else if constexpr (F == kQ6_K) {
-        // 2-byte aligned super-block: 16-bit loads
-        const uint16_t* p = reinterpret_cast<const uint16_t*>(row + 210 * b);
+    } else {
+        // Q4_K (16-byte aligned super-blocks) or Q6_K (2-byte aligned, read
+        // with 16-bit loads) decoded by the unit kernels' block functions
         uint32_t U[54];
+        if constexpr (F == kQ4_K) {
+            const uint4* src = reinterpret_cast<const uint4*>(row + 144 * b);
 #pragma unroll
-        for (int i = 0; i < 52; ++i) U[i] = static_cast<uint32_t>(p[2 * i]) | (static_cast<uint32_t>(p[2 * i + 1]) << 16);
-        U[53] = p[104];
-        const float* xb = x + 256 * b;
+            for (int t = 0; t < 9; ++t) {
+                const uint4 v = src[t];
+                U[4 * t] = v.x; U[4 * t + 1] = v.y; U[4 * t + 2] = v.z; U[4 * t + 3] = v.w;
+            }
+        } else {
+            const uint16_t* p = reinterpret_cast<const uint16_t*>(row + 210 * b);
+#pragma unroll
+            for (int i = 0; i < 52; ++i)
+                U[i] = static_cast<uint32_t>(p[2 * i]) | (static_cast<uint32_t>(p[2 * i + 1]) << 16);
+            U[53] = p[104];
+        }
         float s = 0.f;
         static_for<8>([&](auto kc) {
             constexpr int k = decltype(kc)::value;
-            s += q6_k_block_dot<k>(U, xb + 32 * k);
-        });
-        return 0.25f * s;
-    } else {
-        const uint4* src = reinterpret_cast<const uint4*>(row + 144 * b);
-        uint32_t U[36];
+            float xk[32];
 #pragma unroll
-        for (int t = 0; t < 9; ++t) {
-            const uint4 v = src[t];
-            U[4 * t] = v.x; U[4 * t + 1] = v.y; U[4 * t + 2] = v.z; U[4 * t + 3] = v.w;
-        }
-        const float* xb = x + 256 * b;
-        float s = 0.f;
-        static_for<8>([&](auto jc) {
-            constexpr int j = decltype(jc)::value;
-            s += q4_k_sub_dot<j>(U, xb + 32 * j);
+            for (int i = 0; i < 32; ++i) xk[i] = xa(256 * b + 32 * k + i);
+            if constexpr (F == kQ4_K) s += q4_k_sub_dot<k>(U, xk);
+            else s += q6_k_block_dot<k>(U, xk);
+            asm volatile("" : "+v"(s));  // one block's activations live at a time
         });
-        return s;
+        return s * kRowScale<F>;
     }
 }
 
-template <int F, bool PAIR>
+// Any K % 32 == 0 (K % 256 == 0 for Q4_K and Q6_K).  One wave per row, lanes
+// stride over the row's blocks, activations read from global memory.  Rows
+// need not be 16-byte aligned; Q4_0 / Q8_0 / Q6_K blocks are read with
+// 16-bit loads.
+template <int F, bool PAIR, bool GIN>
 __global__ __launch_bounds__(kBlockThreads)
 void gemv_generic_kernel(const uint8_t* __restrict__ W0, const uint8_t* __restrict__ W1,
-                         const float* __restrict__ x, float* __restrict__ y,
+                         const float* __restrict__ x, const float* __restrict__ xu, float* __restrict__ y,
                          int N, int64_t nblocks, int64_t row_bytes) {
     const int lane = threadIdx.x & (kWave - 1);
     const int wave_stride = gridDim.x * kWavesPerBlock;
+    const ActIn<GIN> xa{x, xu};
     for (int row = blockIdx.x * kWavesPerBlock + threadIdx.x / kWave; row < N; row += wave_stride) {
         float a0 = 0.f, a1 = 0.f;
         for (int64_t b = lane; b < nblocks; b += kWave) {
-            a0 += generic_block_dot<F>(W0 + row * row_bytes, b, x);
-            if constexpr (PAIR) a1 += generic_block_dot<F>(W1 + row * row_bytes, b, x);
+            a0 += generic_block_dot<F, GIN>(W0 + row * row_bytes, b, xa);
+            if constexpr (PAIR) a1 += generic_block_dot<F, GIN>(W1 + row * row_bytes, b, xa);
         }
         a0 = wave_sum(a0);
         if constexpr (PAIR) a1 = wave_sum(a1);
@@ -452,8 +574,8 @@ void gemv_generic_kernel(const uint8_t* __restrict__ W0, const uint8_t* __restri
     }
 }
 
-template <int F, int R, bool PAIR>
-hipError_t launch_unit(const void* W0, const void* W1, const float* x, float* y, int N, int G,
+template <int F, int R, bool PAIR, bool GIN>
+hipError_t launch_unit(const void* W0, const void* W1, const float* x, const float* xu, float* y, int N, int G,
                        hipStream_t stream) {
     const int S = kWave / G;
     const int rows_per_pass = S * R;
@@ -466,25 +588,86 @@ hipError_t launch_unit(const void* W0, const void* W1, const float* x, float* y,
     int blocks = (npasses + kWavesPerBlock - 1) / kWavesPerBlock;
     if (blocks > max_blocks) blocks = max_blocks;
     const size_t lds = static_cast<size_t>(G) * kXsStride * sizeof(float);
-    hipLaunchKernelGGL((gemv_unit_kernel<F, R, PAIR>), dim3(blocks), dim3(kBlockThreads), lds, stream,
-                       static_cast<const uint8_t*>(W0), static_cast<const uint8_t*>(W1), x, y,
+    hipLaunchKernelGGL((gemv_unit_kernel<F, R, PAIR, GIN>), dim3(blocks), dim3(kBlockThreads), lds, stream,
+                       static_cast<const uint8_t*>(W0), static_cast<const uint8_t*>(W1), x, xu, y,
                        N, G, S, npasses);
     return hipGetLastError();
 }
 
-template <int F, bool PAIR>
-hipError_t launch_generic(const void* W0, const void* W1, const float* x, float* y, int N, int64_t K,
-                          hipStream_t stream) {
+// Slicing of a long row for gemv_split_kernel: KS slices of Gs units, S rows
+// per wave, RG row groups per workgroup.
+struct SplitPlan {
+    int KS, Gs, S, RG, npasses, blocks;
+    size_t lds;
+};
+
+// Picks the slice count that keeps the most lanes on real units (ties: fewer
+// slices), up to 16 waves per workgroup.  False if x does not fit in LDS.
+bool plan_split(int G, int N, SplitPlan* p) {
+    int best = 0;
+    double best_eff = -1.0;
+    for (int ks = 2; ks <= 16; ++ks) {
+        const int gs = (G + ks - 1) / ks;
+        if (gs > kWave) continue;
+        const int s = kWave / gs;
+        const double eff = static_cast<double>(s) * G / (static_cast<double>(kWave) * ks);
+        if (eff > best_eff + 1e-9) {
+            best_eff = eff;
+            best = ks;
+        }
+    }
+    if (best == 0) return false;
+    p->KS = best;
+    p->Gs = (G + best - 1) / best;
+    p->S = kWave / p->Gs;
+    p->RG = (kSplitThreads / kWave) / best;
+    p->lds = (static_cast<size_t>(G) * kXsStride + 2 * static_cast<size_t>(p->RG) * p->S * p->KS) * sizeof(float);
+    const size_t max_lds = static_cast<size_t>(device_max_lds());
+    if (p->lds > max_lds) return false;
+    const int rows_per_pass = p->RG * p->S;
+    p->npasses = (N + rows_per_pass - 1) / rows_per_pass;
+    // Resident workgroups per CU: by LDS, and at most two of 16 waves.
+    int per_cu = static_cast<int>(max_lds / p->lds);
+    per_cu = per_cu < 1 ? 1 : (per_cu > 2 ? 2 : per_cu);
+    const int max_blocks = device_cus() * per_cu;
+    p->blocks = p->npasses < max_blocks ? p->npasses : max_blocks;
+    return true;
+}
+
+template <int F, bool GIN>
+hipError_t launch_split(const void* W, const float* x, const float* xu, float* y, int N, int G,
+                        const SplitPlan& p, hipStream_t stream) {
+    hipLaunchKernelGGL((gemv_split_kernel<F, GIN>), dim3(p.blocks), dim3(p.RG * p.KS * kWave), p.lds, stream,
+                       static_cast<const uint8_t*>(W), x, xu, y, N, G, p.KS, p.Gs, p.S, p.RG, p.npasses);
+    return hipGetLastError();
+}
+
+template <int F, bool PAIR, bool GIN>
+hipError_t launch_generic(const void* W0, const void* W1, const float* x, const float* xu, float* y, int N,
+                          int64_t K, hipStream_t stream) {
     const int64_t per = (F == kQ4_K || F == kQ6_K) ? 256 : 32;
     const int64_t bytes = (F == kQ4_0) ? 18 : (F == kQ8_0 ? 34 : (F == kQ4_K ? 144 : 210));
     const int64_t nb = K / per;
     const int max_blocks = device_cus() * 8;
     int blocks = (N + kWavesPerBlock - 1) / kWavesPerBlock;
     if (blocks > max_blocks) blocks = max_blocks;
-    hipLaunchKernelGGL((gemv_generic_kernel<F, PAIR>), dim3(blocks), dim3(kBlockThreads), 0, stream,
-                       static_cast<const uint8_t*>(W0), static_cast<const uint8_t*>(W1), x, y,
+    hipLaunchKernelGGL((gemv_generic_kernel<F, PAIR, GIN>), dim3(blocks), dim3(kBlockThreads), 0, stream,
+                       static_cast<const uint8_t*>(W0), static_cast<const uint8_t*>(W1), x, xu, y,
                        N, nb, nb * bytes);
     return hipGetLastError();
+}
+
+// One format, plain or gated input: unit kernel, split kernel or generic.
+template <int F, bool GIN>
+hipError_t launch_one(const void* W, const float* x, const float* xu, float* y, int N, int64_t K,
+                      hipStream_t stream) {
+    if (K % kUnitElems == 0) {
+        const int G = static_cast<int>(K / kUnitElems);
+        if (G <= kMaxUnits) return launch_unit<F, 1, false, GIN>(W, nullptr, x, xu, y, N, G, stream);
+        SplitPlan p;
+        if (plan_split(G, N, &p)) return launch_split<F, GIN>(W, x, xu, y, N, G, p, stream);
+    }
+    return launch_generic<F, false, GIN>(W, nullptr, x, xu, y, N, K, stream);
 }
 
 }  // namespace
@@ -501,32 +684,41 @@ int device_cus() {
     return cached[dev];
 }
 
-// Largest K the unit kernels take: the padded activation slices must fit in
-// 64 KiB of LDS per workgroup (63 units = 65,520 B).
-constexpr int64_t kUnitMaxG = kMaxUnits;
+int device_max_lds() {
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 65536;
+    if (cached[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess || n <= 0)
+            n = 65536;
+        cached[dev] = n;
+    }
+    return cached[dev];
+}
 
-hipError_t launch_gemv(int fmt, const void* W, const void* W_up, const float* x, float* y,
+hipError_t launch_gemv(int fmt, const void* W, const void* W_up, const float* x, const float* x_up, float* y,
                        int64_t N64, int64_t K, hipStream_t stream) {
     const int N = static_cast<int>(N64);
-    const bool unit = (K % kUnitElems == 0) && (K / kUnitElems <= kUnitMaxG);
-    const int G = static_cast<int>(K / kUnitElems);
     if (W_up != nullptr) {
-        return unit ? launch_unit<kQ4_0, 1, true>(W, W_up, x, y, N, G, stream)
-                    : launch_generic<kQ4_0, true>(W, W_up, x, y, N, K, stream);
+        // the gated pair: gate and up rows of the same shape in one launch
+        const bool unit = (K % kUnitElems == 0) && (K / kUnitElems <= kMaxUnits);
+        return unit ? launch_unit<kQ4_0, 1, true, false>(W, W_up, x, nullptr, y, N, static_cast<int>(K / kUnitElems),
+                                                        stream)
+                    : launch_generic<kQ4_0, true, false>(W, W_up, x, nullptr, y, N, K, stream);
+    }
+    if (x_up != nullptr) {
+        switch (fmt) {
+        case kQ4_0: return launch_one<kQ4_0, true>(W, x, x_up, y, N, K, stream);
+        case kQ4_K: return launch_one<kQ4_K, true>(W, x, x_up, y, N, K, stream);
+        default: return launch_one<kQ6_K, true>(W, x, x_up, y, N, K, stream);
+        }
     }
     switch (fmt) {
-    case kQ4_0:
-        return unit ? launch_unit<kQ4_0, 1, false>(W, nullptr, x, y, N, G, stream)
-                    : launch_generic<kQ4_0, false>(W, nullptr, x, y, N, K, stream);
-    case kQ8_0:
-        return unit ? launch_unit<kQ8_0, 1, false>(W, nullptr, x, y, N, G, stream)
-                    : launch_generic<kQ8_0, false>(W, nullptr, x, y, N, K, stream);
-    case kQ4_K:
-        return unit ? launch_unit<kQ4_K, 1, false>(W, nullptr, x, y, N, G, stream)
-                    : launch_generic<kQ4_K, false>(W, nullptr, x, y, N, K, stream);
-    default:
-        return unit ? launch_unit<kQ6_K, 1, false>(W, nullptr, x, y, N, G, stream)
-                    : launch_generic<kQ6_K, false>(W, nullptr, x, y, N, K, stream);
+    case kQ4_0: return launch_one<kQ4_0, false>(W, x, nullptr, y, N, K, stream);
+    case kQ8_0: return launch_one<kQ8_0, false>(W, x, nullptr, y, N, K, stream);
+    case kQ4_K: return launch_one<kQ4_K, false>(W, x, nullptr, y, N, K, stream);
+    default: return launch_one<kQ6_K, false>(W, x, nullptr, y, N, K, stream);
     }
 }
 

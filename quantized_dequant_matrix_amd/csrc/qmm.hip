@@ -1237,7 +1237,7 @@ hipError_t launch_qmm_f32act(const void* W, const float* x, float* y, int64_t N,
     const F32ActPlan p = plan_f32act(N, K, M);
     if (!p.mfma) {
         for (int64_t m = 0; m < M; ++m) {
-            const hipError_t e = launch_gemv(0, W, nullptr, x + m * K, y + m * N, N, K, stream);
+            const hipError_t e = launch_gemv(0, W, nullptr, x + m * K, nullptr, y + m * N, N, K, stream);
             if (e != hipSuccess) return e;
         }
         return hipSuccess;

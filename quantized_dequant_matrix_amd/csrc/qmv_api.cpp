@@ -40,16 +40,21 @@ int check_shape(int64_t N, int64_t K, int64_t M, int64_t elems, int64_t bytes) {
 
 int launched(hipError_t e) { return e == hipSuccess ? QMV_OK : QMV_ERR_LAUNCH; }
 
-int gemv(int fmt, const void* W, const void* W_up, const float* x, float* y, int64_t N, int64_t K, int64_t M,
-         hipStream_t stream) {
+// W_up: second matrix of the gated pair.  x_up: up activations of the gated
+// input (y = W (gelu(x) * x_up)).  At most one of them is given.
+int gemv(int fmt, const void* W, const void* W_up, const float* x, const float* x_up, float* y, int64_t N,
+         int64_t K, int64_t M, hipStream_t stream) {
     if (!W || !x || !y) return QMV_ERR_NULL;
     const int64_t elems = (fmt >= 2) ? 256 : 32;
     const int64_t bytes = (fmt == 0) ? 18 : (fmt == 1 ? 34 : (fmt == 2 ? 144 : 210));
     int rc = check_shape(N, K, M, elems, bytes);
     if (rc) return rc;
-    if (!aligned(W, 16) || (W_up && !aligned(W_up, 16)) || !aligned(x, 4) || !aligned(y, 4)) return QMV_ERR_ALIGN;
+    if (!aligned(W, 16) || (W_up && !aligned(W_up, 16)) || !aligned(x, 4) || (x_up && !aligned(x_up, 4)) ||
+        !aligned(y, 4))
+        return QMV_ERR_ALIGN;
     for (int64_t m = 0; m < M; ++m) {
-        rc = launched(qmv::launch_gemv(fmt, W, W_up, x + m * K, y + m * N, N, K, stream));
+        rc = launched(qmv::launch_gemv(fmt, W, W_up, x + m * K, x_up ? x_up + m * K : nullptr, y + m * N, N, K,
+                                       stream));
         if (rc) return rc;
     }
     return QMV_OK;
@@ -73,25 +78,43 @@ const char* qmv_status_str(int status) {
 }
 
 int qmv_q4_0(const void* W, const float* x, float* y, int64_t N, int64_t K, int64_t M, hipStream_t stream) {
-    return gemv(0, W, nullptr, x, y, N, K, M, stream);
+    return gemv(0, W, nullptr, x, nullptr, y, N, K, M, stream);
 }
 
 int qmv_q8_0(const void* W, const float* x, float* y, int64_t N, int64_t K, int64_t M, hipStream_t stream) {
-    return gemv(1, W, nullptr, x, y, N, K, M, stream);
+    return gemv(1, W, nullptr, x, nullptr, y, N, K, M, stream);
 }
 
 int qmv_q4_k(const void* W, const float* x, float* y, int64_t N, int64_t K, int64_t M, hipStream_t stream) {
-    return gemv(2, W, nullptr, x, y, N, K, M, stream);
+    return gemv(2, W, nullptr, x, nullptr, y, N, K, M, stream);
 }
 
 int qmv_q6_k(const void* W, const float* x, float* y, int64_t N, int64_t K, int64_t M, hipStream_t stream) {
-    return gemv(3, W, nullptr, x, y, N, K, M, stream);
+    return gemv(3, W, nullptr, x, nullptr, y, N, K, M, stream);
 }
 
 int qmv_q4_0_geglu(const void* W_gate, const void* W_up, const float* x, float* h, int64_t N, int64_t K,
                    int64_t M, hipStream_t stream) {
     if (!W_up) return QMV_ERR_NULL;
-    return gemv(0, W_gate, W_up, x, h, N, K, M, stream);
+    return gemv(0, W_gate, W_up, x, nullptr, h, N, K, M, stream);
+}
+
+int qmv_q4_0_geglu_down(const void* W_down, const float* g, const float* u, float* y, int64_t N, int64_t K, int64_t M,
+                        hipStream_t stream) {
+    if (!u) return QMV_ERR_NULL;
+    return gemv(0, W_down, nullptr, g, u, y, N, K, M, stream);
+}
+
+int qmv_q4_k_geglu_down(const void* W_down, const float* g, const float* u, float* y, int64_t N, int64_t K, int64_t M,
+                        hipStream_t stream) {
+    if (!u) return QMV_ERR_NULL;
+    return gemv(2, W_down, nullptr, g, u, y, N, K, M, stream);
+}
+
+int qmv_q6_k_geglu_down(const void* W_down, const float* g, const float* u, float* y, int64_t N, int64_t K, int64_t M,
+                        hipStream_t stream) {
+    if (!u) return QMV_ERR_NULL;
+    return gemv(3, W_down, nullptr, g, u, y, N, K, M, stream);
 }
 
 size_t qmm_q4_0_q8act_ws_bytes(int64_t N, int64_t K, int64_t M) {
@@ -154,7 +177,7 @@ int logits_topk(const void* W_q8_0, const float* x, float* top_val, int32_t* top
     if (!aligned(W_q8_0, 16) || !aligned(x, 4)) return QMV_ERR_ALIGN;
     float* y = static_cast<float*>(ws);
     for (int64_t m = 0; m < M; ++m) {
-        rc = launched(qmv::launch_gemv(1, W_q8_0, nullptr, x + m * K, y + m * N, N, K, stream));
+        rc = launched(qmv::launch_gemv(1, W_q8_0, nullptr, x + m * K, nullptr, y + m * N, N, K, stream));
         if (rc) return rc;
     }
     return launched(qmv::launch_topk(y, top_val, top_idx, N, M, k, softcap, ws, stream));
@@ -182,7 +205,7 @@ int logits_sample(const void* W_q8_0, const float* x, const float* u, int32_t* t
     if (!aligned(W_q8_0, 16) || !aligned(x, 4)) return QMV_ERR_ALIGN;
     float* y = static_cast<float*>(ws);
     for (int64_t m = 0; m < M; ++m) {
-        rc = launched(qmv::launch_gemv(1, W_q8_0, nullptr, x + m * K, y + m * N, N, K, stream));
+        rc = launched(qmv::launch_gemv(1, W_q8_0, nullptr, x + m * K, nullptr, y + m * N, N, K, stream));
         if (rc) return rc;
     }
     rc = launched(qmv::launch_topk(y, top_val, top_idx, N, M, k, softcap, ws, stream));

@@ -12,10 +12,14 @@ namespace qmv {
 // Compute units of the current device (cached per device id).
 int device_cus();
 
+// Largest dynamic LDS per workgroup of the current device (cached).
+int device_max_lds();
+
 // One matrix-vector product (one activation row).  fmt: 0 Q4_0, 1 Q8_0,
 // 2 Q4_K, 3 Q6_K.  W_up != nullptr selects the gated pair (Q4_0 only):
-// y = gelu(W x) * (W_up x).
-hipError_t launch_gemv(int fmt, const void* W, const void* W_up, const float* x, float* y,
+// y = gelu(W x) * (W_up x).  x_up != nullptr selects the gated input
+// (Q4_0, Q4_K, Q6_K): y = W (gelu(x) * x_up).
+hipError_t launch_gemv(int fmt, const void* W, const void* W_up, const float* x, const float* x_up, float* y,
                        int64_t N, int64_t K, hipStream_t stream);
 
 // Top-k over y[M][N] (float32), candidates in ws.

@@ -32,6 +32,9 @@ _SIGS = {
     "qmv_q4_k": ([_P, _P, _P, _I64, _I64, _I64, _P], ctypes.c_int),
     "qmv_q6_k": ([_P, _P, _P, _I64, _I64, _I64, _P], ctypes.c_int),
     "qmv_q4_0_geglu": ([_P, _P, _P, _P, _I64, _I64, _I64, _P], ctypes.c_int),
+    "qmv_q4_0_geglu_down": ([_P, _P, _P, _P, _I64, _I64, _I64, _P], ctypes.c_int),
+    "qmv_q4_k_geglu_down": ([_P, _P, _P, _P, _I64, _I64, _I64, _P], ctypes.c_int),
+    "qmv_q6_k_geglu_down": ([_P, _P, _P, _P, _I64, _I64, _I64, _P], ctypes.c_int),
     "qmm_q4_0_q8act_ws_bytes": ([_I64, _I64, _I64], _SZ),
     "qmm_q4_0_q8act": ([_P, _P, _P, _I64, _I64, _I64, _P, _SZ, _P], ctypes.c_int),
     "qmm_q4_0_f32act_ws_bytes": ([_I64, _I64, _I64], _SZ),
@@ -104,6 +107,18 @@ def qmv_q6_k(W, x, y, N, K, M=1, stream=None):
 
 def qmv_q4_0_geglu(W_gate, W_up, x, h, N, K, M=1, stream=None):
     _call("qmv_q4_0_geglu", _ptr(W_gate), _ptr(W_up), _ptr(x), _ptr(h), N, K, M, _stream(stream))
+
+
+def qmv_q4_0_geglu_down(W_down, g, u, y, N, K, M=1, stream=None):
+    _call("qmv_q4_0_geglu_down", _ptr(W_down), _ptr(g), _ptr(u), _ptr(y), N, K, M, _stream(stream))
+
+
+def qmv_q4_k_geglu_down(W_down, g, u, y, N, K, M=1, stream=None):
+    _call("qmv_q4_k_geglu_down", _ptr(W_down), _ptr(g), _ptr(u), _ptr(y), N, K, M, _stream(stream))
+
+
+def qmv_q6_k_geglu_down(W_down, g, u, y, N, K, M=1, stream=None):
+    _call("qmv_q6_k_geglu_down", _ptr(W_down), _ptr(g), _ptr(u), _ptr(y), N, K, M, _stream(stream))
 
 
 def qmm_q4_0_q8act_ws_bytes(N, K, M) -> int:

@@ -26,7 +26,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported_and_bound():
     names = declared_functions()
-    assert "qmv_q4_0" in names and "logits_topk" in names and len(names) == 17
+    assert "qmv_q4_0" in names and "logits_topk" in names and len(names) == 20
     for n in names:
         assert hasattr(qmv.lib, n), n
     assert sorted(qmv.EXPORTS) == names
@@ -87,6 +87,20 @@ def test_geglu_validation():
     assert call("qmv_q4_0_geglu", None, FAKE, FAKE, FAKE, 8, 256, 1, S) == NUL
     assert call("qmv_q4_0_geglu", FAKE, FAKE + 4, FAKE, FAKE, 8, 256, 1, S) == ALIGN
     assert call("qmv_q4_0_geglu", FAKE, FAKE, FAKE, FAKE, 8, 48, 1, S) == SHAPE
+
+
+@pytest.mark.parametrize("name", ["qmv_q4_0_geglu_down", "qmv_q4_k_geglu_down", "qmv_q6_k_geglu_down"])
+def test_geglu_down_validation(name):
+    assert call(name, None, FAKE, FAKE, FAKE, 8, 256, 1, S) == NUL
+    assert call(name, FAKE, None, FAKE, FAKE, 8, 256, 1, S) == NUL
+    assert call(name, FAKE, FAKE, None, FAKE, 8, 256, 1, S) == NUL
+    assert call(name, FAKE, FAKE, FAKE, None, 8, 256, 1, S) == NUL
+    assert call(name, FAKE + 8, FAKE, FAKE, FAKE, 8, 256, 1, S) == ALIGN
+    assert call(name, FAKE, FAKE, FAKE + 2, FAKE, 8, 256, 1, S) == ALIGN
+    assert call(name, FAKE, FAKE, FAKE, FAKE, 0, 256, 1, S) == SHAPE
+    assert call(name, FAKE, FAKE, FAKE, FAKE, 8, 48, 1, S) == SHAPE
+    if name != "qmv_q4_0_geglu_down":
+        assert call(name, FAKE, FAKE, FAKE, FAKE, 8, 288, 1, S) == SHAPE
 
 
 def test_qmm_validation_and_workspace():

@@ -100,6 +100,52 @@ def test_unit_vectors_give_columns(fmt, K):
     assert np.array_equal(y, ref)
 
 
+# Rows longer than 63 units take the split kernel (K sliced across the
+# waves of a workgroup): 64 and 65 units, the FFN down shape's 84 (with row
+# tails around its 12 rows per pass), the largest K whose activations fit in
+# LDS (157 units) and one past it (generic kernel).
+LONG = [(37, 16384), (41, 16640), (1, 21504), (12, 21504), (13, 21504), (29, 21504), (13, 40192), (11, 40448)]
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("N,K", LONG)
+def test_long_rows(fmt, N, K):
+    seed = 3 * N + K
+    say(f"qmv_{fmt} long rows N={N} K={K} seed={seed}")
+    W, x = synth.problem(fmt, N, K, 1, seed)
+    y = run_gemv(fmt, W, x, N, K)
+    yr, S = oracle.qmv(fmt, W, N, K, x)
+    assert_within(y, yr, oracle.float_tol(S), f"qmv_{fmt} {N}x{K}")
+
+
+@pytest.mark.parametrize("name,fmt", [("c4", "q4_0"), ("q4k_down", "q4_k"), ("q6k_down", "q6_k")])
+def test_down_shape_full(name, fmt):
+    c = synth.CONFIGS[name]
+    say(f"qmv_{fmt} down shape {c['N']}x{c['K']}")
+    W, x = synth.config_problem(name, M=1)
+    y = run_gemv(fmt, W, x, c["N"], c["K"])
+    yr, S = oracle.qmv(fmt, W, c["N"], c["K"], x)
+    w = assert_within(y, yr, oracle.float_tol(S), name)
+    say(f"{name}: worst err/tol {w:.3g}")
+
+
+def test_long_rows_deterministic_and_batched():
+    N, K, M = 300, 21504, 2
+    say("qmv_q6_k split kernel: M=2, 5 repeats bit-identical")
+    qmv = _qmv()
+    W, x = synth.problem("q6_k", N, K, M, 5)
+    Wd, xd = dev(W), dev(x)
+    outs = []
+    for _ in range(5):
+        y = empty((M, N))
+        qmv.qmv_q6_k(Wd, xd, y, N, K, M)
+        outs.append(host(y))
+    for o in outs[1:]:
+        assert np.array_equal(o, outs[0])
+    yr, S = oracle.qmv("q6_k", W, N, K, x, M=M)
+    assert_within(outs[0], yr, oracle.float_tol(S), "split M=2")
+
+
 def test_q6_k_extreme_codes_and_scales():
     # q in {0, 63} and scales in {-128, 127}: the largest products the
     # signed-byte decode forms; rows alternate the super-block alignment
