@@ -280,6 +280,29 @@ def measure_rows(torch, qmv, synth, dev):
                                                                    "GB/s": b / ms / 1e6}
         del slots
 
+    # Attention projections of a Q4_K_M model (Q, K in Q4_K, V in Q6_K): one
+    # launch, and the three single-matrix launches it replaces; 16 slots
+    # (442 MB, past the 256 MB last-level cache)
+    c = synth.CONFIGS["qkv"]
+    Wq, Wk, Wv, x = synth.qkv_problem()
+    sl = [(t(Wq), t(Wk), t(Wv)) for _ in range(16)]
+    xd = t(x)
+    yq, yk, yv = (torch.empty((1, n), device=dev) for n in (c["Nq"], c["Nk"], c["Nv"]))
+    K = c["K"]
+    b = Wq.nbytes + Wk.nbytes + Wv.nbytes + K * 4 + (c["Nq"] + c["Nk"] + c["Nv"]) * 4
+    ms = _time_loop(torch, lambda i: qmv.qmv_q4_k_q6_k_qkv(*sl[i % 16], xd, yq, yk, yv, c["Nq"], c["Nk"], c["Nv"],
+                                                          K, 1), 200)
+    res["qkv_q4_k_q6_k_4096+2048+2048x5376_one_launch"] = {"us": ms * 1e3, "bytes": b, "GB/s": b / ms / 1e6}
+
+    def three(i):
+        a, k_, v_ = sl[i % 16]
+        qmv.qmv_q4_k(a, xd, yq, c["Nq"], K, 1)
+        qmv.qmv_q4_k(k_, xd, yk, c["Nk"], K, 1)
+        qmv.qmv_q6_k(v_, xd, yv, c["Nv"], K, 1)
+    ms = _time_loop(torch, three, 200)
+    res["qkv_q4_k_q6_k_4096+2048+2048x5376_three_launches"] = {"us": ms * 1e3, "bytes": b, "GB/s": b / ms / 1e6}
+    del sl
+
     # C4: Q4_0 x Q8 activations, 5376 x 21504, M = 1, 16, 512; 8 slots
     c = synth.CONFIGS["c4"]
     N, K = c["N"], c["K"]

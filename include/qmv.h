@@ -130,6 +130,19 @@ int qmv_q4_k_geglu_down(const void* W_down, const float* g, const float* u, floa
 int qmv_q6_k_geglu_down(const void* W_down, const float* g, const float* u, float* y,
                         int64_t N, int64_t K, int64_t M, hipStream_t stream);
 
+/* The attention input projections of a Q4_K_M model in one launch:
+ *   q[m] = Wq x[m], k[m] = Wk x[m] (Q4_K, [Nq][K] and [Nk][K]),
+ *   v[m] = Wv x[m] (Q6_K, [Nv][K]),
+ * outputs float32 [M][Nq], [M][Nk], [M][Nv].  K % 256 == 0.  Each output
+ * row is the same product qmv_q4_k / qmv_q6_k form for that row.
+ * Rows longer than 16128 weights take one launch per matrix.
+ * [captable section 2: q4k_q6k_qkv_proj, Q4_K Q/K + Q6_K V x f32 in one
+ *  dispatch, and the route that selects it for the (Q4_K, Q4_K, Q6_K) mix;
+ *  finding F2: a QKV route must honour V's own format] */
+int qmv_q4_k_q6_k_qkv(const void* Wq, const void* Wk, const void* Wv, const float* x,
+                      float* q, float* k, float* v, int64_t Nq, int64_t Nk, int64_t Nv,
+                      int64_t K, int64_t M, hipStream_t stream);
+
 /* Q4_0 weights times Q8-quantized activations, y float32 [M][N].
  * Step 1 quantizes each 32-element block of x (float32 arithmetic):
  *   amax = max|x|, d_x = amax / 127 (IEEE division),

@@ -304,9 +304,10 @@ constexpr int kUnitWords = UnitInfo<F>::kVec * 4 + (F == kQ6_K ? 2 : 0);
 // acc[i] = the sum over unit i's 256 weights of (decoded weight) * x, for NR
 // units held in U that share the activation slice xw (LDS), times the
 // format's 1/kRowScale.
-template <int F, int NR>
-__device__ __forceinline__ void dot_units(uint32_t (&U)[NR][kUnitWords<F>], const uint32_t (&sh)[NR],
+template <int F, int NR, int UW>
+__device__ __forceinline__ void dot_units(uint32_t (&U)[NR][UW], const uint32_t (&sh)[NR],
                                           const float* xw, float (&acc)[NR]) {
+    static_assert(UW >= kUnitWords<F>, "unit words");
 #pragma unroll
     for (int i = 0; i < NR; ++i) acc[i] = 0.f;
     if constexpr (F == kQ6_K) {
@@ -400,6 +401,79 @@ void gemv_unit_kernel(const uint8_t* __restrict__ W0, const uint8_t* __restrict_
                 if (active && u == 0 && row0 + r < N) y[row0 + r] = v0;
             }
         }
+        pass += wave_stride;
+        if (pass < npasses) load(pass);
+    }
+}
+
+// ------------------------------------------------------- three-matrix kernel
+// Three matrices that share x and K (G = K/256 <= 63 units) in one launch:
+// the attention input projections of a Q4_K_M model, Q and K rows in format
+// FA and V rows in format FB.  The passes of the three matrices form one
+// index space (V's first: its units are the largest, so the launch ends on
+// the cheaper ones); a wave takes passes like the unit kernel and decodes
+// with the format of the pass's matrix (a wave-uniform branch).
+template <int FA, int FB>
+__global__ __launch_bounds__(kBlockThreads)
+void gemv_qkv_kernel(const uint8_t* __restrict__ Wq, const uint8_t* __restrict__ Wk, const uint8_t* __restrict__ Wv,
+                     const float* __restrict__ x, float* __restrict__ yq, float* __restrict__ yk,
+                     float* __restrict__ yv, int Nq, int Nk, int Nv, int G, int S, int Pv, int Pq, int Pk) {
+    constexpr int UWMAX = kUnitWords<FA> > kUnitWords<FB> ? kUnitWords<FA> : kUnitWords<FB>;
+    extern __shared__ float xs[];
+    const int lane = threadIdx.x & (kWave - 1);
+    const int seg = lane / G;
+    const int u = lane - seg * G;
+    const bool active = seg < S;
+    const int64_t rbA = static_cast<int64_t>(G) * UnitInfo<FA>::kBytes;
+    const int64_t rbB = static_cast<int64_t>(G) * UnitInfo<FB>::kBytes;
+    const int npasses = Pv + Pq + Pk;
+    const int wave_stride = gridDim.x * kWavesPerBlock;
+    int pass = blockIdx.x * kWavesPerBlock + (threadIdx.x / kWave);
+
+    uint32_t U[1][UWMAX];
+    uint32_t sh[1];
+    auto load = [&](int p) {
+        if (p < Pv) {
+            int row = p * S + seg;
+            row = row < Nv ? row : Nv - 1;
+            load_unit<FB>(U[0], sh[0], Wv + row * rbB + u * UnitInfo<FB>::kBytes);
+        } else {
+            const bool isq = p < Pv + Pq;
+            const int n = isq ? Nq : Nk;
+            int row = (p - (isq ? Pv : Pv + Pq)) * S + seg;
+            row = row < n ? row : n - 1;
+            load_unit<FA>(U[0], sh[0], (isq ? Wq : Wk) + row * rbA + u * UnitInfo<FA>::kBytes);
+        }
+    };
+
+    if (pass < npasses) load(pass);
+    stage_x<false>(xs, x, nullptr, G, kBlockThreads);
+    __syncthreads();
+
+    while (pass < npasses) {
+        int xoff = u * kXsStride;
+        asm volatile("" : "+v"(xoff));
+        const float* xw = xs + xoff;
+        float acc[1];
+        float* yo;
+        int n, row;
+        float scale;
+        if (pass < Pv) {
+            dot_units<FB, 1>(U, sh, xw, acc);
+            yo = yv;
+            n = Nv;
+            row = pass * S + seg;
+            scale = kRowScale<FB>;
+        } else {
+            dot_units<FA, 1>(U, sh, xw, acc);
+            const bool isq = pass < Pv + Pq;
+            yo = isq ? yq : yk;
+            n = isq ? Nq : Nk;
+            row = (pass - (isq ? Pv : Pv + Pq)) * S + seg;
+            scale = kRowScale<FA>;
+        }
+        const float v = segment_sum(acc[0], u, G) * scale;
+        if (active && u == 0 && row < n) yo[row] = v;
         pass += wave_stride;
         if (pass < npasses) load(pass);
     }
@@ -720,6 +794,32 @@ hipError_t launch_gemv(int fmt, const void* W, const void* W_up, const float* x,
     case kQ4_K: return launch_one<kQ4_K, false>(W, x, nullptr, y, N, K, stream);
     default: return launch_one<kQ6_K, false>(W, x, nullptr, y, N, K, stream);
     }
+}
+
+hipError_t launch_qkv(const void* Wq, const void* Wk, const void* Wv, const float* x, float* yq, float* yk, float* yv,
+                      int64_t Nq, int64_t Nk, int64_t Nv, int64_t K, hipStream_t stream) {
+    const int G = static_cast<int>(K / kUnitElems);
+    if (G > kMaxUnits) {
+        // long rows: one split-kernel launch per matrix
+        hipError_t e = launch_one<kQ4_K, false>(Wq, x, nullptr, yq, static_cast<int>(Nq), K, stream);
+        if (e == hipSuccess) e = launch_one<kQ4_K, false>(Wk, x, nullptr, yk, static_cast<int>(Nk), K, stream);
+        if (e == hipSuccess) e = launch_one<kQ6_K, false>(Wv, x, nullptr, yv, static_cast<int>(Nv), K, stream);
+        return e;
+    }
+    const int S = kWave / G;
+    const int Pq = static_cast<int>((Nq + S - 1) / S);
+    const int Pk = static_cast<int>((Nk + S - 1) / S);
+    const int Pv = static_cast<int>((Nv + S - 1) / S);
+    const int npasses = Pq + Pk + Pv;
+    const int max_blocks = device_cus() * 3;
+    int blocks = (npasses + kWavesPerBlock - 1) / kWavesPerBlock;
+    if (blocks > max_blocks) blocks = max_blocks;
+    const size_t lds = static_cast<size_t>(G) * kXsStride * sizeof(float);
+    hipLaunchKernelGGL((gemv_qkv_kernel<kQ4_K, kQ6_K>), dim3(blocks), dim3(kBlockThreads), lds, stream,
+                       static_cast<const uint8_t*>(Wq), static_cast<const uint8_t*>(Wk),
+                       static_cast<const uint8_t*>(Wv), x, yq, yk, yv, static_cast<int>(Nq), static_cast<int>(Nk),
+                       static_cast<int>(Nv), G, S, Pv, Pq, Pk);
+    return hipGetLastError();
 }
 
 }  // namespace qmv

@@ -117,6 +117,24 @@ int qmv_q6_k_geglu_down(const void* W_down, const float* g, const float* u, floa
     return gemv(3, W_down, nullptr, g, u, y, N, K, M, stream);
 }
 
+int qmv_q4_k_q6_k_qkv(const void* Wq, const void* Wk, const void* Wv, const float* x, float* q, float* k, float* v,
+                      int64_t Nq, int64_t Nk, int64_t Nv, int64_t K, int64_t M, hipStream_t stream) {
+    if (!Wq || !Wk || !Wv || !x || !q || !k || !v) return QMV_ERR_NULL;
+    int rc = check_shape(Nq, K, M, 256, 144);
+    if (!rc) rc = check_shape(Nk, K, M, 256, 144);
+    if (!rc) rc = check_shape(Nv, K, M, 256, 210);
+    if (rc) return rc;
+    if (!aligned(Wq, 16) || !aligned(Wk, 16) || !aligned(Wv, 16) || !aligned(x, 4) || !aligned(q, 4) ||
+        !aligned(k, 4) || !aligned(v, 4))
+        return QMV_ERR_ALIGN;
+    for (int64_t m = 0; m < M; ++m) {
+        rc = launched(qmv::launch_qkv(Wq, Wk, Wv, x + m * K, q + m * Nq, k + m * Nk, v + m * Nv, Nq, Nk, Nv, K,
+                                      stream));
+        if (rc) return rc;
+    }
+    return QMV_OK;
+}
+
 size_t qmm_q4_0_q8act_ws_bytes(int64_t N, int64_t K, int64_t M) {
     if (check_shape(N, K, M, 32, 18) != QMV_OK) return 0;
     return qmv::qmm_ws_bytes(N, K, M);

@@ -22,6 +22,11 @@ int device_max_lds();
 hipError_t launch_gemv(int fmt, const void* W, const void* W_up, const float* x, const float* x_up, float* y,
                        int64_t N, int64_t K, hipStream_t stream);
 
+// Q and K (Q4_K) and V (Q6_K) rows of one activation row in one launch
+// (K % 256 == 0; rows longer than 63 units take one launch per matrix).
+hipError_t launch_qkv(const void* Wq, const void* Wk, const void* Wv, const float* x, float* yq, float* yk, float* yv,
+                      int64_t Nq, int64_t Nk, int64_t Nv, int64_t K, hipStream_t stream);
+
 // Top-k over y[M][N] (float32), candidates in ws.
 size_t topk_ws_bytes(int64_t N, int64_t M, int k);
 hipError_t launch_topk(const float* y, float* top_val, int32_t* top_idx, int64_t N, int64_t M,

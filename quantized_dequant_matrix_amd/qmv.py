@@ -35,6 +35,7 @@ _SIGS = {
     "qmv_q4_0_geglu_down": ([_P, _P, _P, _P, _I64, _I64, _I64, _P], ctypes.c_int),
     "qmv_q4_k_geglu_down": ([_P, _P, _P, _P, _I64, _I64, _I64, _P], ctypes.c_int),
     "qmv_q6_k_geglu_down": ([_P, _P, _P, _P, _I64, _I64, _I64, _P], ctypes.c_int),
+    "qmv_q4_k_q6_k_qkv": ([_P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I64, _P], ctypes.c_int),
     "qmm_q4_0_q8act_ws_bytes": ([_I64, _I64, _I64], _SZ),
     "qmm_q4_0_q8act": ([_P, _P, _P, _I64, _I64, _I64, _P, _SZ, _P], ctypes.c_int),
     "qmm_q4_0_f32act_ws_bytes": ([_I64, _I64, _I64], _SZ),
@@ -119,6 +120,11 @@ def qmv_q4_k_geglu_down(W_down, g, u, y, N, K, M=1, stream=None):
 
 def qmv_q6_k_geglu_down(W_down, g, u, y, N, K, M=1, stream=None):
     _call("qmv_q6_k_geglu_down", _ptr(W_down), _ptr(g), _ptr(u), _ptr(y), N, K, M, _stream(stream))
+
+
+def qmv_q4_k_q6_k_qkv(Wq, Wk, Wv, x, q, k, v, Nq, Nk, Nv, K, M=1, stream=None):
+    _call("qmv_q4_k_q6_k_qkv", _ptr(Wq), _ptr(Wk), _ptr(Wv), _ptr(x), _ptr(q), _ptr(k), _ptr(v), Nq, Nk, Nv, K, M,
+          _stream(stream))
 
 
 def qmm_q4_0_q8act_ws_bytes(N, K, M) -> int:

@@ -225,6 +225,9 @@ CONFIGS = {
     "q6k_gate": dict(fmt="q6_k", N=21504, K=5376, M=1),
     "q6k_down": dict(fmt="q6_k", N=5376, K=21504, M=1),
     "q4k_down": dict(fmt="q4_k", N=5376, K=21504, M=1),
+    # attention input projections of a Q4_K_M model at the 5376 embedding:
+    # 32 query heads and 16 key/value heads of 128 (Q, K in Q4_K, V in Q6_K)
+    "qkv": dict(Nq=4096, Nk=2048, Nv=2048, K=5376, M=1),
 }
 
 
@@ -232,6 +235,17 @@ def config_problem(name: str, M: int | None = None):
     c = CONFIGS[name]
     m = M if M is not None else c.get("M", 1)
     return problem(c["fmt"], c["N"], c["K"], m, SEEDS[name])
+
+
+def qkv_problem():
+    """(Wq, Wk, Wv, x) of the attention projection workload: Q4_K Q and K,
+    Q6_K V, each matrix from its own seed offset, x from the first."""
+    c = CONFIGS["qkv"]
+    seed = SEEDS["qkv"]
+    Wq, x = problem("q4_k", c["Nq"], c["K"], 1, seed)
+    Wk = q4_k_weights(c["Nk"], c["K"], seed + 1000)
+    Wv = q6_k_weights(c["Nv"], c["K"], seed + 2000)
+    return Wq, Wk, Wv, x
 
 
 def gate_up_problem():

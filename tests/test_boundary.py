@@ -26,7 +26,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported_and_bound():
     names = declared_functions()
-    assert "qmv_q4_0" in names and "logits_topk" in names and len(names) == 20
+    assert "qmv_q4_0" in names and "logits_topk" in names and len(names) == 21
     for n in names:
         assert hasattr(qmv.lib, n), n
     assert sorted(qmv.EXPORTS) == names
@@ -101,6 +101,25 @@ def test_geglu_down_validation(name):
     assert call(name, FAKE, FAKE, FAKE, FAKE, 8, 48, 1, S) == SHAPE
     if name != "qmv_q4_0_geglu_down":
         assert call(name, FAKE, FAKE, FAKE, FAKE, 8, 288, 1, S) == SHAPE
+
+
+def test_qkv_validation():
+    args = [FAKE] * 7 + [8, 4, 4, 256, 1, S]
+
+    def with_(i, v):
+        a = list(args)
+        a[i] = v
+        return call("qmv_q4_k_q6_k_qkv", *a)
+
+    for i in range(7):
+        assert with_(i, None) == NUL
+    for i in range(3):
+        assert with_(i, FAKE + 8) == ALIGN
+    for i in range(3, 7):
+        assert with_(i, FAKE + 2) == ALIGN
+    assert with_(7, 0) == SHAPE and with_(8, 0) == SHAPE and with_(9, 0) == SHAPE
+    assert with_(10, 288) == SHAPE and with_(10, 32) == SHAPE
+    assert with_(11, 0) == SHAPE
 
 
 def test_qmm_validation_and_workspace():
