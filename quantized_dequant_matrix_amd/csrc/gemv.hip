@@ -526,6 +526,11 @@ void gemv_split_kernel(const uint8_t* __restrict__ W, const float* __restrict__ 
         asm volatile("" : "+v"(xoff));
         float acc[1];
         dot_units<F, 1>(U, sh, xs + xoff, acc);
+        // The weights of this pass are consumed: start the next pass's loads
+        // before the barrier, so that HBM is not idle while the workgroup
+        // waits for its slowest wave.
+        const int next = pass + gridDim.x;
+        if (next < npasses) load(next);
         const float v = segment_sum(live ? acc[0] : 0.f, uu, Gs);
         if (seg < S && uu == 0) red[((buf * RG + rg) * S + seg) * KS + kq] = v;
         __syncthreads();
@@ -541,8 +546,7 @@ void gemv_split_kernel(const uint8_t* __restrict__ W, const float* __restrict__ 
         // after the next pass's barrier, which every reader above passes
         // after its reads.
         buf ^= 1;
-        pass += gridDim.x;
-        if (pass < npasses) load(pass);
+        pass = next;
     }
 }
 
