@@ -57,6 +57,12 @@ def _load():
     lib.oracle_gelu_tanh.argtypes = [ctypes.c_double]
     lib.oracle_gelu_tanh.restype = ctypes.c_double
     lib.oracle_geglu.argtypes = [P, P, I64, P]
+    lib.oracle_e2m1_to_f64.argtypes = [ctypes.c_int]
+    lib.oracle_e2m1_to_f64.restype = ctypes.c_double
+    lib.oracle_e8m0_to_f64.argtypes = [ctypes.c_int]
+    lib.oracle_e8m0_to_f64.restype = ctypes.c_double
+    lib.oracle_dequant_mxfp4_row.argtypes = [P, P, I64, P]
+    lib.oracle_qmv_mxfp4.argtypes = [P, P, I64, I64, P, I64, P, I64, P, P]
     lib.oracle_qmv_geglu_down.argtypes = [ctypes.c_int, P, I64, I64, P, P, I64, P, I64, P, P, P]
     lib.oracle_softcap.argtypes = [P, I64, ctypes.c_double, P]
     lib.oracle_quantize_q8.argtypes = [P, I64, I64, P, P]
@@ -131,6 +137,41 @@ def qmv(fmt: str, W: np.ndarray, N: int, K: int, x: np.ndarray, M: int = 1, rows
                             None if r is None else _ptr(r), nrows, _ptr(y), _ptr(S))
     if rc:
         raise ValueError(f"oracle_qmv failed ({rc})")
+    return y, S
+
+
+def e2m1(code: int) -> float:
+    return float(_load().oracle_e2m1_to_f64(int(code)))
+
+
+def e8m0(e: int) -> float:
+    return float(_load().oracle_e8m0_to_f64(int(e)))
+
+
+def dequant_mxfp4_row(codes: np.ndarray, scales: np.ndarray, K: int) -> np.ndarray:
+    codes = np.ascontiguousarray(codes, dtype=np.uint8).reshape(-1)
+    scales = np.ascontiguousarray(scales, dtype=np.uint8).reshape(-1)
+    if K % 32 or codes.size != K // 2 or scales.size != K // 32:
+        raise ValueError("shape mismatch")
+    w = np.empty(K, dtype=np.float64)
+    _load().oracle_dequant_mxfp4_row(_ptr(codes), _ptr(scales), K, _ptr(w))
+    return w
+
+
+def qmv_mxfp4(codes: np.ndarray, scales: np.ndarray, N: int, K: int, x: np.ndarray, M: int = 1, rows=None):
+    """float64 y[M, nrows] and S = sum |w x| for an MXFP4 matrix (two planes)."""
+    codes = np.ascontiguousarray(codes).view(np.uint8).reshape(-1)
+    scales = np.ascontiguousarray(scales).view(np.uint8).reshape(-1)
+    x = np.ascontiguousarray(x, dtype=np.float32).reshape(-1)
+    if K % 32 or codes.size != N * K // 2 or scales.size != N * K // 32 or x.size != M * K:
+        raise ValueError("shape mismatch")
+    r, nrows = _rows_arg(rows, N)
+    y = np.empty((M, nrows), dtype=np.float64)
+    S = np.empty((M, nrows), dtype=np.float64)
+    rc = _load().oracle_qmv_mxfp4(_ptr(codes), _ptr(scales), N, K, _ptr(x), M,
+                                  None if r is None else _ptr(r), nrows, _ptr(y), _ptr(S))
+    if rc:
+        raise ValueError(f"oracle_qmv_mxfp4 failed ({rc})")
     return y, S
 
 

@@ -170,6 +170,99 @@ static void dequant_q6_k_block(const uint8_t* b, double* w) {
     }
 }
 
+/* ------------------------------------------------------------------ */
+/* MXFP4 [captable section 1: mxfp4_matvec, "MXFP4 16B/32 + ext e8m0   */
+/* scales"; roadmap K5: a weight layout whose decode maps to native     */
+/* packed operations].  Two planes per matrix:                          */
+/*   codes  [N][K/32][16 B]: 32 four-bit E2M1 elements per block,       */
+/*   scales [N][K/32] bytes: one E8M0 exponent per block.               */
+/* Reading (the pages give the sizes and the word "ext" only):          */
+/*   element 2i of a block is the low nibble of code byte i, element     */
+/*   2i+1 its high nibble (the consecutive-pair order of MX checkpoints  */
+/*   stored as separate block and scale tensors);                       */
+/*   E2M1 (OCP Microscaling formats): sign bit, 2 exponent bits with     */
+/*   bias 1, 1 mantissa bit; exponent 0 is subnormal (m * 2^-1), no      */
+/*   infinities or NaNs;                                                 */
+/*   E8M0: 2^(e - 127), e = 255 is NaN;                                  */
+/*   w = E2M1(code) * E8M0(scale).                                       */
+/* Pinned in tests/test_oracle_mxfp4.py: E8M0 against torch's           */
+/* float8_e8m0fnu for all 256 bytes, E2M1 against a generic minifloat   */
+/* decoder that is itself checked on numpy's float16 and torch's        */
+/* float8_e4m3fn, element order and plane layout on hand-built blocks.  */
+/* ------------------------------------------------------------------ */
+double oracle_e2m1_to_f64(int code) {
+    int sign = (code >> 3) & 1;
+    int e = (code >> 1) & 3;
+    int m = code & 1;
+    double v = (e == 0) ? ldexp((double)m, -1) : ldexp(1.0 + 0.5 * (double)m, e - 1);
+    return sign ? -v : v;
+}
+
+double oracle_e8m0_to_f64(int e) {
+    return (e == 255) ? NAN : ldexp(1.0, e - 127);
+}
+
+int64_t oracle_mxfp4_plane_bytes(int64_t K, int64_t* scale_bytes) {
+    if (K % 32) return -1;
+    if (scale_bytes) *scale_bytes = K / 32;
+    return (K / 32) * 16;
+}
+
+/* One row: codes row (K/2 bytes), scales row (K/32 bytes). */
+int oracle_dequant_mxfp4_row(const uint8_t* codes, const uint8_t* scales, int64_t K, double* w) {
+    if (K % 32) return -1;
+    for (int64_t b = 0; b < K / 32; ++b) {
+        double s = oracle_e8m0_to_f64(scales[b]);
+        for (int i = 0; i < 16; ++i) {
+            uint8_t byte = codes[16 * b + i];
+            w[32 * b + 2 * i] = oracle_e2m1_to_f64(byte & 0x0f) * s;
+            w[32 * b + 2 * i + 1] = oracle_e2m1_to_f64(byte >> 4) * s;
+        }
+    }
+    return 0;
+}
+
+/* y[m][i] = sum_k w[r_i][k] x[m][k], S = sum |w x|, as oracle_qmv, for an
+ * MXFP4 matrix given as its two planes. */
+int oracle_qmv_mxfp4(const uint8_t* codes, const uint8_t* scales, int64_t N, int64_t K,
+                     const float* x, int64_t M, const int64_t* rows, int64_t nrows,
+                     double* y, double* S) {
+    if (K % 32) return -1;
+    if (rows == NULL) nrows = N;
+    for (int64_t i = 0; i < nrows; ++i) {
+        int64_t r = rows ? rows[i] : i;
+        if (r < 0 || r >= N) return -2;
+    }
+    int bad = 0;
+#pragma omp parallel
+    {
+        double* w = (double*)malloc(sizeof(double) * (size_t)K);
+        if (!w) {
+#pragma omp atomic write
+            bad = 1;
+        }
+#pragma omp for schedule(static)
+        for (int64_t i = 0; i < nrows; ++i) {
+            if (!w) continue;
+            int64_t r = rows ? rows[i] : i;
+            oracle_dequant_mxfp4_row(codes + r * (K / 2), scales + r * (K / 32), K, w);
+            for (int64_t m = 0; m < M; ++m) {
+                const float* xm = x + m * K;
+                double acc = 0.0, sabs = 0.0;
+                for (int64_t k = 0; k < K; ++k) {
+                    double p = w[k] * (double)xm[k];
+                    acc += p;
+                    sabs += fabs(p);
+                }
+                y[m * nrows + i] = acc;
+                if (S) S[m * nrows + i] = sabs;
+            }
+        }
+        free(w);
+    }
+    return bad ? -3 : 0;
+}
+
 /* Dequantize one row of K weights to float64.  Returns 0, or -1 on a bad
  * format / K. */
 int oracle_dequant_row(int fmt, const uint8_t* row, int64_t K, double* w) {

@@ -19,6 +19,9 @@ Value distributions (the synthetic stand-ins for real model weights):
   Q6_K: d = fp16(|N(0,1)| * 0.0001) (about half of them fp16 subnormals,
         as in real Q6_K tensors), sub-block scales uniform int8 in
         -128..127, 6-bit q uniform in 0..63 (w = d s (q - 32))
+  MXFP4 (two planes): E8M0 block exponents uniform in 116..124 (scales
+        2^-11 .. 2^-3), E2M1 codes as whole uniform random bytes (every
+        4-bit code, -0 included, uniform)
   x:    f32 ~ N(0,1)
 N(0,1) is drawn in float32, scaled in float32 and rounded to fp16 by numpy
 (round to nearest even, subnormals kept).  4-bit codes are drawn as whole
@@ -35,6 +38,8 @@ Byte layouts (GGUF block formats, as loaded by the pages' engines):
   Q6_K (210 B / 256): 128 bytes ql | 64 bytes qh | 16 int8 scales | fp16 d;
         element 128h+32g+l: low (g < 2) or high (g >= 2) nibble of
         ql[64h+32(g%2)+l], two high bits at bits 2g, 2g+1 of qh[32h+l]
+  MXFP4: codes [N][K/32][16 B], element 2i in the low and 2i+1 in the high
+        nibble of byte i; scales [N][K/32], one E8M0 byte per block
 """
 from __future__ import annotations
 
@@ -46,7 +51,8 @@ BLOCK_ELEMS = {"q4_0": 32, "q8_0": 32, "q4_k": 256, "q6_k": 256}
 # Seeds of the five workloads; the up-projection matrix of the gated pair
 # uses its own seed.
 SEEDS = {"c1": 101, "c2": 102, "c2_up": 1102, "c3": 103, "c4": 104, "c5": 105,
-         "q6k_gate": 106, "q6k_down": 107, "qkv": 108, "q4k_down": 109}
+         "q6k_gate": 106, "q6k_down": 107, "qkv": 108, "q4k_down": 109, "mxfp4_gate": 110,
+         "mxfp4_down": 111}
 
 
 def row_bytes(fmt: str, K: int) -> int:
@@ -196,6 +202,25 @@ def q6_k_weights(N: int, K: int, seed: int, rng=None) -> np.ndarray:
     return out.reshape(-1)
 
 
+def mxfp4_weights(N: int, K: int, seed: int, rng=None):
+    """(codes uint8[N * K/2], scales uint8[N * K/32]): block exponents first,
+    then the code bytes."""
+    rng = rng or _rng(seed)
+    if K % 32:
+        raise ValueError(f"K={K} is not a multiple of 32 for mxfp4")
+    nb = N * (K // 32)
+    scales = rng.integers(116, 125, size=nb, dtype=np.uint8)
+    codes = _random_bytes(rng, nb * 16)
+    return codes, scales
+
+
+def mxfp4_problem(N: int, K: int, M: int, seed: int):
+    rng = _rng(seed)
+    codes, scales = mxfp4_weights(N, K, seed, rng=rng)
+    x = activations(M, K, seed, rng=rng)
+    return codes, scales, x
+
+
 def activations(M: int, K: int, seed: int, rng=None) -> np.ndarray:
     rng = rng or _rng(seed)
     return rng.standard_normal(M * K, dtype=np.float32).reshape(M, K)
@@ -228,6 +253,9 @@ CONFIGS = {
     # attention input projections of a Q4_K_M model at the 5376 embedding:
     # 32 query heads and 16 key/value heads of 128 (Q, K in Q4_K, V in Q6_K)
     "qkv": dict(Nq=4096, Nk=2048, Nv=2048, K=5376, M=1),
+    # MXFP4 at the FFN gate and down shapes
+    "mxfp4_gate": dict(fmt="mxfp4", N=21504, K=5376, M=1),
+    "mxfp4_down": dict(fmt="mxfp4", N=5376, K=21504, M=1),
 }
 
 
