@@ -280,6 +280,17 @@ def measure_rows(torch, qmv, synth, dev):
                                                                    "GB/s": b / ms / 1e6}
         del slots
 
+    # MXFP4 (codes and E8M0 scales in two planes) at the gate and down shapes, 8 slots
+    for name in ("mxfp4_gate", "mxfp4_down"):
+        c = synth.CONFIGS[name]
+        codes, scales, x = synth.mxfp4_problem(c["N"], c["K"], 1, synth.SEEDS[name])
+        sl = [(t(codes), t(scales)) for _ in range(8)]
+        xd, y = t(x), torch.empty((1, c["N"]), device=dev)
+        ms = _time_loop(torch, lambda i: qmv.qmv_mxfp4(*sl[i % 8], xd, y, c["N"], c["K"], 1), 100)
+        b = codes.nbytes + scales.nbytes + c["K"] * 4 + c["N"] * 4
+        res[f"{name}_qmv_mxfp4_{c['N']}x{c['K']}"] = {"us": ms * 1e3, "bytes": b, "GB/s": b / ms / 1e6}
+        del sl
+
     # Attention projections of a Q4_K_M model (Q, K in Q4_K, V in Q6_K): one
     # launch, and the three single-matrix launches it replaces; 16 slots
     # (442 MB, past the 256 MB last-level cache)

@@ -102,6 +102,21 @@ int qmv_q4_k(const void* W, const float* x, float* y,
 int qmv_q6_k(const void* W, const float* x, float* y,
              int64_t N, int64_t K, int64_t M, hipStream_t stream);
 
+/* As qmv_q4_0 for MXFP4 weights held in two planes:
+ *   W_codes  [N][K/32][16 B]: 32 E2M1 elements per block, element 2i in the
+ *            low and 2i+1 in the high nibble of byte i (E2M1: sign, two
+ *            exponent bits with bias 1, one mantissa bit; values
+ *            +-{0, 0.5, 1, 1.5, 2, 3, 4, 6});
+ *   W_scales [N][K/32]: one E8M0 byte e per block, scale 2^(e - 127)
+ *            (e = 255 is NaN and makes the row's output NaN);
+ *   w = E2M1(code) * 2^(e - 127).  K % 32 == 0; both planes 16-byte
+ *   aligned.  The codes are converted with gfx950's packed FP4 conversion.
+ * [captable section 1: mxfp4_matvec, MXFP4 16 B / 32 + external e8m0
+ *  scales x f32; roadmap K5: a weight layout whose decode maps to native
+ *  packed operations] */
+int qmv_mxfp4(const void* W_codes, const void* W_scales, const float* x, float* y,
+              int64_t N, int64_t K, int64_t M, hipStream_t stream);
+
 /* Gated GELU projection pair: h[m][n] = gelu(g) * u with g = W_gate x[m],
  * u = W_up x[m], both Q4_0 [N][K], gelu the tanh form
  * v/2 (1 + tanh(sqrt(2/pi) (v + 0.044715 v^3))).  Both matrices are read

@@ -1,5 +1,6 @@
-// Fused-dequant matrix-vector kernels for Q4_0, Q8_0, Q4_K and Q6_K weights
-// with float32 activations and float32 accumulation, and the gated GELU pair.
+// Fused-dequant matrix-vector kernels for Q4_0, Q8_0, Q4_K, Q6_K and MXFP4
+// weights with float32 activations and float32 accumulation, and the gated
+// GELU pair.
 //
 // What is computed: y[n] = sum_k w[n][k] x[k] with w decoded from the block
 // formats on the fly ["Gemma 4 M4 Max kernel roadmap", K2 step 1: direct
@@ -31,6 +32,10 @@
 //         bits with shifts and one mask-merge per 4 weights, then one
 //         byte-select convert per weight; each 16-weight partial sum is
 //         scaled by d*scale (exact) and the row sum by 1/4 (exact).
+//   MXFP4: gfx950's packed FP4 conversion (v_cvt_scalef32_pk_f32_fp4) turns
+//         one code byte into its two float32 values (exact) -- one op per
+//         two weights -- then one FMA per weight; each 32-weight sum is
+//         multiplied by its E8M0 scale 2^(e - 127) (exact, power of two).
 // So every product carries at most the rounding of float32 arithmetic on
 // the exact weight, and the float32 sums stay within 1e-5 * sum|w x|.
 #include <utility>
@@ -184,12 +189,50 @@ __device__ __forceinline__ void q6_k_realign(uint32_t* U, uint32_t sh) {
     U[0] = __builtin_amdgcn_perm(U[0], U[52] << 16, sel);
 }
 
+// ---------------------------------------------------------------- MXFP4
+// Block k (0..7) of an MXFP4 unit U[34]: code dwords 4k .. 4k+3 (element 2i
+// in the low and 2i+1 in the high nibble of code byte i), E8M0 scale bytes
+// in U[32], U[33].  The conversion runs at scale 1.0 (exponent 127, i.e.
+// 2^0); the block's own scale multiplies the block sum.
+typedef float v2f_t __attribute__((ext_vector_type(2)));
+
+// E8M0 exponent byte -> float32 2^(e - 127): e = 0 is 2^-127 (a float32
+// subnormal), e = 255 is NaN.
+__device__ __forceinline__ float e8m0_to_float(uint32_t e) {
+    const uint32_t bits = (e == 0) ? 0x00400000u : (e == 255 ? 0x7FC00000u : (e << 23));
+    return __builtin_bit_cast(float, bits);
+}
+
+template <int k>
+__device__ __forceinline__ float mxfp4_block_dot(const uint32_t* U, const float* xk) {
+    float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        const uint32_t c = U[4 * k + t];
+        const v2f_t p0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c, 1.0f, 0);
+        const v2f_t p1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c, 1.0f, 1);
+        const v2f_t p2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c, 1.0f, 2);
+        const v2f_t p3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c, 1.0f, 3);
+        s0 = fmaf(p0[0], xk[8 * t + 0], s0);
+        s1 = fmaf(p0[1], xk[8 * t + 1], s1);
+        s0 = fmaf(p1[0], xk[8 * t + 2], s0);
+        s1 = fmaf(p1[1], xk[8 * t + 3], s1);
+        s0 = fmaf(p2[0], xk[8 * t + 4], s0);
+        s1 = fmaf(p2[1], xk[8 * t + 5], s1);
+        s0 = fmaf(p3[0], xk[8 * t + 6], s0);
+        s1 = fmaf(p3[1], xk[8 * t + 7], s1);
+    }
+    const uint32_t e = (U[32 + (k >> 2)] >> (8 * (k & 3))) & 0xffu;
+    return (s0 + s1) * e8m0_to_float(e);
+}
+
 template <int F, int k>
 __device__ __forceinline__ float unit_block_dot(const uint32_t* U, const float* xk) {
     if constexpr (F == kQ4_0) return q4_0_block_dot<k>(U, xk);
     else if constexpr (F == kQ8_0) return q8_0_block_dot<k>(U, xk);
     else if constexpr (F == kQ4_K) return q4_k_sub_dot<k>(U, xk);
-    else return q6_k_block_dot<k>(U, xk);
+    else if constexpr (F == kQ6_K) return q6_k_block_dot<k>(U, xk);
+    else return mxfp4_block_dot<k>(U, xk);
 }
 
 // Factor that turns a row's sum of unit_block_dot results into y.
@@ -263,8 +306,10 @@ __device__ __forceinline__ void stage_x(float* xs, const float* __restrict__ x, 
 // One lane's 256-weight unit at base: UnitInfo<F>::kVec 16-byte loads into
 // U (and, for Q6_K, the 16-bit rest into U[52] and the super-block's offset
 // past its dword into sh; q6_k_realign then puts the words in place).
+// sbase: MXFP4 only, the unit's 8 scale bytes in the scale plane.
 template <int F>
-__device__ __forceinline__ void load_unit(uint32_t* U, uint32_t& sh, const uint8_t* base) {
+__device__ __forceinline__ void load_unit(uint32_t* U, uint32_t& sh, const uint8_t* base,
+                                          const uint8_t* sbase = nullptr) {
     constexpr int VEC = UnitInfo<F>::kVec;
     if constexpr (F == kQ6_K) {
         // W is 16-byte aligned and super-blocks are 210 B, so a super-block
@@ -295,11 +340,20 @@ __device__ __forceinline__ void load_unit(uint32_t* U, uint32_t& sh, const uint8
             U[4 * t + 2] = v.z;
             U[4 * t + 3] = v.w;
         }
+        if constexpr (F == kMXFP4) {
+            const uint2 sc = *reinterpret_cast<const uint2*>(sbase);
+            U[32] = sc.x;
+            U[33] = sc.y;
+        }
     }
 }
 
 template <int F>
-constexpr int kUnitWords = UnitInfo<F>::kVec * 4 + (F == kQ6_K ? 2 : 0);
+constexpr int kUnitWords = UnitInfo<F>::kVec * 4 + ((F == kQ6_K || F == kMXFP4) ? 2 : 0);
+
+// Bytes of a unit's scales in a separate scale plane (MXFP4), else 0.
+template <int F>
+constexpr int kUnitScaleBytes = (F == kMXFP4) ? 8 : 0;
 
 // acc[i] = the sum over unit i's 256 weights of (decoded weight) * x, for NR
 // units held in U that share the activation slice xw (LDS), times the
@@ -369,9 +423,15 @@ void gemv_unit_kernel(const uint8_t* __restrict__ W0, const uint8_t* __restrict_
             // last row again: valid memory, results never stored.
             int row = (p * S + seg) * R + r;
             row = row < N ? row : N - 1;
+            if constexpr (F == kMXFP4) {
+                // W0: code plane, W1: scale plane
+                load_unit<F>(U[r], sh[r], W0 + row * row_bytes + u * UB,
+                             W1 + static_cast<int64_t>(row) * G * kUnitScaleBytes<F> + u * kUnitScaleBytes<F>);
+            } else {
 #pragma unroll
-            for (int m = 0; m < NM; ++m)
-                load_unit<F>(U[m * R + r], sh[m * R + r], (m == 0 ? W0 : W1) + row * row_bytes + u * UB);
+                for (int m = 0; m < NM; ++m)
+                    load_unit<F>(U[m * R + r], sh[m * R + r], (m == 0 ? W0 : W1) + row * row_bytes + u * UB);
+            }
         }
     };
 
@@ -490,8 +550,9 @@ constexpr int kSplitThreads = 1024;
 
 template <int F, bool GIN>
 __global__ __launch_bounds__(kSplitThreads)
-void gemv_split_kernel(const uint8_t* __restrict__ W, const float* __restrict__ x, const float* __restrict__ xu,
-                       float* __restrict__ y, int N, int G, int KS, int Gs, int S, int RG, int npasses) {
+void gemv_split_kernel(const uint8_t* __restrict__ W, const uint8_t* __restrict__ Ws, const float* __restrict__ x,
+                       const float* __restrict__ xu, float* __restrict__ y, int N, int G, int KS, int Gs, int S,
+                       int RG, int npasses) {
     constexpr int UB = UnitInfo<F>::kBytes;
     extern __shared__ float xs[];
     float* red = xs + G * kXsStride;  // [2][RG][S][KS] slice sums, double-buffered by pass
@@ -512,7 +573,8 @@ void gemv_split_kernel(const uint8_t* __restrict__ W, const float* __restrict__ 
     auto load = [&](int p) {
         int row = (p * RG + rg) * S + seg;
         row = row < N ? row : N - 1;
-        load_unit<F>(U[0], sh[0], W + row * row_bytes + uc * UB);
+        load_unit<F>(U[0], sh[0], W + row * row_bytes + uc * UB,
+                     Ws + (static_cast<int64_t>(row) * G + uc) * kUnitScaleBytes<F>);
     };
 
     int pass = blockIdx.x;
@@ -563,9 +625,20 @@ struct ActIn {
     }
 };
 
+// srow: MXFP4 only, the row's scale bytes (one per block).
 template <int F, bool GIN>
-__device__ __forceinline__ float generic_block_dot(const uint8_t* __restrict__ row, int64_t b, ActIn<GIN> xa) {
-    if constexpr (F == kQ4_0) {
+__device__ __forceinline__ float generic_block_dot(const uint8_t* __restrict__ row, int64_t b, ActIn<GIN> xa,
+                                                   const uint8_t* __restrict__ srow) {
+    if constexpr (F == kMXFP4) {
+        const uint4 c = reinterpret_cast<const uint4*>(row)[b];
+        uint32_t U[34];
+        U[0] = c.x; U[1] = c.y; U[2] = c.z; U[3] = c.w;
+        U[32] = srow[b];
+        float xk[32];
+#pragma unroll
+        for (int i = 0; i < 32; ++i) xk[i] = xa(32 * b + i);
+        return mxfp4_block_dot<0>(U, xk);
+    } else if constexpr (F == kQ4_0) {
         const uint16_t* p = reinterpret_cast<const uint16_t*>(row + 18 * b);
         const float d = half_bits_to_float(p[0]);
         const int64_t xb = 32 * b;
@@ -639,9 +712,11 @@ void gemv_generic_kernel(const uint8_t* __restrict__ W0, const uint8_t* __restri
     const ActIn<GIN> xa{x, xu};
     for (int row = blockIdx.x * kWavesPerBlock + threadIdx.x / kWave; row < N; row += wave_stride) {
         float a0 = 0.f, a1 = 0.f;
+        // MXFP4: W1 is the scale plane, one byte per block
+        const uint8_t* srow = (F == kMXFP4) ? W1 + row * nblocks : nullptr;
         for (int64_t b = lane; b < nblocks; b += kWave) {
-            a0 += generic_block_dot<F, GIN>(W0 + row * row_bytes, b, xa);
-            if constexpr (PAIR) a1 += generic_block_dot<F, GIN>(W1 + row * row_bytes, b, xa);
+            a0 += generic_block_dot<F, GIN>(W0 + row * row_bytes, b, xa, srow);
+            if constexpr (PAIR) a1 += generic_block_dot<F, GIN>(W1 + row * row_bytes, b, xa, nullptr);
         }
         a0 = wave_sum(a0);
         if constexpr (PAIR) a1 = wave_sum(a1);
@@ -713,10 +788,11 @@ bool plan_split(int G, int N, SplitPlan* p) {
 }
 
 template <int F, bool GIN>
-hipError_t launch_split(const void* W, const float* x, const float* xu, float* y, int N, int G,
+hipError_t launch_split(const void* W, const void* Ws, const float* x, const float* xu, float* y, int N, int G,
                         const SplitPlan& p, hipStream_t stream) {
     hipLaunchKernelGGL((gemv_split_kernel<F, GIN>), dim3(p.blocks), dim3(p.RG * p.KS * kWave), p.lds, stream,
-                       static_cast<const uint8_t*>(W), x, xu, y, N, G, p.KS, p.Gs, p.S, p.RG, p.npasses);
+                       static_cast<const uint8_t*>(W), static_cast<const uint8_t*>(Ws), x, xu, y, N, G, p.KS, p.Gs,
+                       p.S, p.RG, p.npasses);
     return hipGetLastError();
 }
 
@@ -724,7 +800,7 @@ template <int F, bool PAIR, bool GIN>
 hipError_t launch_generic(const void* W0, const void* W1, const float* x, const float* xu, float* y, int N,
                           int64_t K, hipStream_t stream) {
     const int64_t per = (F == kQ4_K || F == kQ6_K) ? 256 : 32;
-    const int64_t bytes = (F == kQ4_0) ? 18 : (F == kQ8_0 ? 34 : (F == kQ4_K ? 144 : 210));
+    const int64_t bytes = (F == kQ4_0) ? 18 : (F == kQ8_0 ? 34 : (F == kQ4_K ? 144 : (F == kQ6_K ? 210 : 16)));
     const int64_t nb = K / per;
     const int max_blocks = device_cus() * 8;
     int blocks = (N + kWavesPerBlock - 1) / kWavesPerBlock;
@@ -736,16 +812,17 @@ hipError_t launch_generic(const void* W0, const void* W1, const float* x, const 
 }
 
 // One format, plain or gated input: unit kernel, split kernel or generic.
+// Ws: the scale plane (MXFP4), else nullptr.
 template <int F, bool GIN>
 hipError_t launch_one(const void* W, const float* x, const float* xu, float* y, int N, int64_t K,
-                      hipStream_t stream) {
+                      hipStream_t stream, const void* Ws = nullptr) {
     if (K % kUnitElems == 0) {
         const int G = static_cast<int>(K / kUnitElems);
-        if (G <= kMaxUnits) return launch_unit<F, 1, false, GIN>(W, nullptr, x, xu, y, N, G, stream);
+        if (G <= kMaxUnits) return launch_unit<F, 1, false, GIN>(W, Ws, x, xu, y, N, G, stream);
         SplitPlan p;
-        if (plan_split(G, N, &p)) return launch_split<F, GIN>(W, x, xu, y, N, G, p, stream);
+        if (plan_split(G, N, &p)) return launch_split<F, GIN>(W, Ws, x, xu, y, N, G, p, stream);
     }
-    return launch_generic<F, false, GIN>(W, nullptr, x, xu, y, N, K, stream);
+    return launch_generic<F, false, GIN>(W, Ws, x, xu, y, N, K, stream);
 }
 
 }  // namespace
@@ -798,6 +875,11 @@ hipError_t launch_gemv(int fmt, const void* W, const void* W_up, const float* x,
     case kQ4_K: return launch_one<kQ4_K, false>(W, x, nullptr, y, N, K, stream);
     default: return launch_one<kQ6_K, false>(W, x, nullptr, y, N, K, stream);
     }
+}
+
+hipError_t launch_gemv_mxfp4(const void* codes, const void* scales, const float* x, float* y, int64_t N, int64_t K,
+                             hipStream_t stream) {
+    return launch_one<kMXFP4, false>(codes, x, nullptr, y, static_cast<int>(N), K, stream, scales);
 }
 
 hipError_t launch_qkv(const void* Wq, const void* Wk, const void* Wv, const float* x, float* yq, float* yk, float* yv,

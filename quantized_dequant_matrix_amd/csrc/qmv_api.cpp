@@ -93,6 +93,19 @@ int qmv_q6_k(const void* W, const float* x, float* y, int64_t N, int64_t K, int6
     return gemv(3, W, nullptr, x, nullptr, y, N, K, M, stream);
 }
 
+int qmv_mxfp4(const void* W_codes, const void* W_scales, const float* x, float* y, int64_t N, int64_t K, int64_t M,
+              hipStream_t stream) {
+    if (!W_codes || !W_scales || !x || !y) return QMV_ERR_NULL;
+    int rc = check_shape(N, K, M, 32, 17);  // 16 code bytes + 1 scale byte per block
+    if (rc) return rc;
+    if (!aligned(W_codes, 16) || !aligned(W_scales, 16) || !aligned(x, 4) || !aligned(y, 4)) return QMV_ERR_ALIGN;
+    for (int64_t m = 0; m < M; ++m) {
+        rc = launched(qmv::launch_gemv_mxfp4(W_codes, W_scales, x + m * K, y + m * N, N, K, stream));
+        if (rc) return rc;
+    }
+    return QMV_OK;
+}
+
 int qmv_q4_0_geglu(const void* W_gate, const void* W_up, const float* x, float* h, int64_t N, int64_t K,
                    int64_t M, hipStream_t stream) {
     if (!W_up) return QMV_ERR_NULL;

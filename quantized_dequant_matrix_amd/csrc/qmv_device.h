@@ -21,7 +21,7 @@ constexpr int kUnitElems = 256;
 // so that lanes holding consecutive units start on different LDS banks.
 constexpr int kXsStride = kUnitElems + 4;
 
-enum Format : int { kQ4_0 = 0, kQ8_0 = 1, kQ4_K = 2, kQ6_K = 3 };
+enum Format : int { kQ4_0 = 0, kQ8_0 = 1, kQ4_K = 2, kQ6_K = 3, kMXFP4 = 4 };
 
 template <int F> struct UnitInfo;
 template <> struct UnitInfo<kQ4_0> { static constexpr int kBytes = 144; static constexpr int kVec = 9; };
@@ -31,6 +31,10 @@ template <> struct UnitInfo<kQ4_K> { static constexpr int kBytes = 144; static c
 // the 13 dword-aligned 16-byte pieces from the dword at or before its start
 // and two 16-bit words at its end, then realigns (see gemv.hip).
 template <> struct UnitInfo<kQ6_K> { static constexpr int kBytes = 210; static constexpr int kVec = 13; };
+
+// MXFP4 keeps codes and scales in two planes: a unit is 8 blocks, i.e. 128
+// code bytes (kBytes, kVec below) plus 8 scale bytes from the scale plane.
+template <> struct UnitInfo<kMXFP4> { static constexpr int kBytes = 128; static constexpr int kVec = 8; };
 
 // 16-byte vector with 4-byte alignment: one global_load_dwordx4 from an
 // address that is only dword aligned.

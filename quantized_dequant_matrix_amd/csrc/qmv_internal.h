@@ -22,6 +22,10 @@ int device_max_lds();
 hipError_t launch_gemv(int fmt, const void* W, const void* W_up, const float* x, const float* x_up, float* y,
                        int64_t N, int64_t K, hipStream_t stream);
 
+// MXFP4: code plane [N][K/32][16 B] and scale plane [N][K/32] (E8M0).
+hipError_t launch_gemv_mxfp4(const void* codes, const void* scales, const float* x, float* y, int64_t N, int64_t K,
+                             hipStream_t stream);
+
 // Q and K (Q4_K) and V (Q6_K) rows of one activation row in one launch
 // (K % 256 == 0; rows longer than 63 units take one launch per matrix).
 hipError_t launch_qkv(const void* Wq, const void* Wk, const void* Wv, const float* x, float* yq, float* yk, float* yv,

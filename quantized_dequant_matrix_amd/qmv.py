@@ -31,6 +31,7 @@ _SIGS = {
     "qmv_q8_0": ([_P, _P, _P, _I64, _I64, _I64, _P], ctypes.c_int),
     "qmv_q4_k": ([_P, _P, _P, _I64, _I64, _I64, _P], ctypes.c_int),
     "qmv_q6_k": ([_P, _P, _P, _I64, _I64, _I64, _P], ctypes.c_int),
+    "qmv_mxfp4": ([_P, _P, _P, _P, _I64, _I64, _I64, _P], ctypes.c_int),
     "qmv_q4_0_geglu": ([_P, _P, _P, _P, _I64, _I64, _I64, _P], ctypes.c_int),
     "qmv_q4_0_geglu_down": ([_P, _P, _P, _P, _I64, _I64, _I64, _P], ctypes.c_int),
     "qmv_q4_k_geglu_down": ([_P, _P, _P, _P, _I64, _I64, _I64, _P], ctypes.c_int),
@@ -104,6 +105,10 @@ def qmv_q4_k(W, x, y, N, K, M=1, stream=None):
 
 def qmv_q6_k(W, x, y, N, K, M=1, stream=None):
     _call("qmv_q6_k", _ptr(W), _ptr(x), _ptr(y), N, K, M, _stream(stream))
+
+
+def qmv_mxfp4(W_codes, W_scales, x, y, N, K, M=1, stream=None):
+    _call("qmv_mxfp4", _ptr(W_codes), _ptr(W_scales), _ptr(x), _ptr(y), N, K, M, _stream(stream))
 
 
 def qmv_q4_0_geglu(W_gate, W_up, x, h, N, K, M=1, stream=None):

@@ -26,7 +26,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported_and_bound():
     names = declared_functions()
-    assert "qmv_q4_0" in names and "logits_topk" in names and len(names) == 21
+    assert "qmv_q4_0" in names and "logits_topk" in names and len(names) == 22
     for n in names:
         assert hasattr(qmv.lib, n), n
     assert sorted(qmv.EXPORTS) == names
@@ -101,6 +101,19 @@ def test_geglu_down_validation(name):
     assert call(name, FAKE, FAKE, FAKE, FAKE, 8, 48, 1, S) == SHAPE
     if name != "qmv_q4_0_geglu_down":
         assert call(name, FAKE, FAKE, FAKE, FAKE, 8, 288, 1, S) == SHAPE
+
+
+def test_mxfp4_validation():
+    c = lambda *a: call("qmv_mxfp4", *a)
+    assert c(None, FAKE, FAKE, FAKE, 8, 256, 1, S) == NUL
+    assert c(FAKE, None, FAKE, FAKE, 8, 256, 1, S) == NUL
+    assert c(FAKE, FAKE, None, FAKE, 8, 256, 1, S) == NUL
+    assert c(FAKE, FAKE, FAKE, None, 8, 256, 1, S) == NUL
+    assert c(FAKE + 8, FAKE, FAKE, FAKE, 8, 256, 1, S) == ALIGN
+    assert c(FAKE, FAKE + 8, FAKE, FAKE, 8, 256, 1, S) == ALIGN
+    assert c(FAKE, FAKE, FAKE + 2, FAKE, 8, 256, 1, S) == ALIGN
+    assert c(FAKE, FAKE, FAKE, FAKE, 8, 48, 1, S) == SHAPE
+    assert c(FAKE, FAKE, FAKE, FAKE, 0, 64, 1, S) == SHAPE
 
 
 def test_qkv_validation():
