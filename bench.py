@@ -37,8 +37,8 @@ sys.path.insert(0, ROOT)
 TRAFFIC_PROFILE = os.path.join("profiles", "qmv_bench_workloads_hbm_traffic.md")
 # kernel symbol of each timed launch, and its workgroups per CU at most
 KERNEL_OF = {
-    "qmv_q4_0": ("qmv::gemv_unit_kernel<0, 1, false>", 3),
-    "qmv_q4_0_geglu": ("qmv::gemv_unit_kernel<0, 1, true>", 4),
+    "qmv_q4_0": ("qmv::gemv_unit_kernel<0, 1, false, false>", 3),
+    "qmv_q4_0_geglu": ("qmv::gemv_unit_kernel<0, 1, true, false>", 4),
 }
 
 
