@@ -13,17 +13,26 @@
 // in round r-1": no per-element bookkeeping is needed.
 //
 // Stage 1: every wave owns a chunk of 64 KPL entries (KPL keys per lane, in
-//          registers) and emits its k best, largest first; a round is a
-//          lane-local masked maximum (a tree over KPL keys) plus a DPP wave
-//          reduction, with no workgroup barrier.  KPL grows with N so that
-//          there are at most 1024 chunks.
-// Stage 2: one 1024-thread workgroup per activation row runs a tournament
-//          over the sorted chunk lists in two levels: thread t holds the head
-//          of list t (and the next few entries in registers); each wave takes
-//          the k best of its 64 lists (a wave maximum per round, the lane that
-//          owned it moves to its next entry: keys are unique, so exactly one
-//          lane wins a round), then wave 0 takes the k best of the 16 wave
-//          lists the same way.  No round needs a workgroup barrier.
+//          registers) and emits its k best, largest first.  For k <= 16 a
+//          round is a lane-local masked maximum (a tree over KPL keys) plus
+//          a DPP wave maximum, k rounds in all.  For larger k (with 4 keys
+//          per lane, rows up to 262,144 entries) the wave sorts its 256 keys
+//          with a bitonic network, at a cost that does not grow with k
+//          (cross-lane steps are DPP moves and gfx950's permlane swaps).
+//          KPL grows with N so that there are at most 1024 chunks.
+// Stage 2: one 1024-thread workgroup per activation row.
+//   k <= 16: a tournament over the sorted chunk lists in two levels: thread
+//          t holds the head of list t (and the next few entries in
+//          registers); each wave takes the k best of its 64 lists (a wave
+//          maximum per round, the lane that owned it moves to its next
+//          entry: keys are unique, so exactly one lane wins a round), then
+//          wave 0 takes the k best of the 16 wave lists the same way.
+//   k > 16: the list heads (each list's largest key) are sorted; T = the
+//          k-th largest head.  At least k keys (those heads) are >= T, so
+//          the k-th largest key overall is >= T and only keys >= T can win;
+//          they lie in the k lists whose heads are >= T, at most k^2 keys
+//          (about k for logits).  Those candidates are sorted and the first
+//          k written.
 // Very long rows (more than 4M entries, so more than 1024 chunks of 4096)
 // fall back to a merge that rescans candidates from memory every round.
 #include <stdint.h>
@@ -37,7 +46,14 @@ namespace {
 constexpr int kMergeThreads = 1024;
 constexpr int kMergeWaves = kMergeThreads / kWave;
 constexpr int kMaxLists = kMergeThreads;  // chunk lists the tournament takes
-constexpr int kListRegs = 8;              // entries of its list a merge thread keeps in registers
+constexpr int kMaxCand = 64 * 64;         // candidates of stage 2: at most k^2, k <= 64
+constexpr int kListRegs = 8;              // entries of its list a tournament thread keeps in registers
+// Up to this k the selection runs k rounds (a wave maximum each); above it
+// the chunks are sorted and stage 2 selects by threshold, whose cost does
+// not grow with k.  Measured at 262,144 logits: k = 10 takes 13.0 us with
+// rounds and 15.9 us sorted, k = 40 takes 35 us with rounds and 17 us
+// sorted.
+constexpr int kRoundsMaxK = 16;
 
 __device__ __forceinline__ uint64_t order_key(float v, uint32_t idx) {
     uint32_t code;
@@ -92,6 +108,119 @@ __device__ __forceinline__ uint64_t wave_max64(uint64_t v) {
     return (static_cast<uint64_t>(hi) << 32) | lo;
 }
 
+__device__ __forceinline__ uint64_t umin64(uint64_t a, uint64_t b) { return a < b ? a : b; }
+
+// v of lane ^ d, for d = 1, 2, 4, 8, 16, 32 (a constant once the sorting
+// loops are unrolled), without the LDS crossbar: DPP quad permutes for 1 and
+// 2, two row shifts for 4, a row rotation for 8, and gfx950's row and
+// half-wave swaps for 16 and 32.
+__device__ __forceinline__ uint32_t xor_lanes(uint32_t v, int d) {
+    const int lane = threadIdx.x & (kWave - 1);
+    switch (d) {
+    case 1: return static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(v), 0xB1, 0xF, 0xF, false));
+    case 2: return static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(v), 0x4E, 0xF, 0xF, false));
+    case 4: {
+        const uint32_t up = static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(v), 0x104, 0xF, 0xF, false));
+        const uint32_t dn = static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(v), 0x114, 0xF, 0xF, false));
+        return (lane & 4) ? dn : up;
+    }
+    case 8: return static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(v), 0x128, 0xF, 0xF, false));
+    case 16: {
+        const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+        return ((lane >> 4) & 1) ? r[0] : r[1];
+    }
+    default: {
+        const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+        return (lane >= 32) ? r[0] : r[1];
+    }
+    }
+}
+
+__device__ __forceinline__ uint64_t shfl_xor64(uint64_t v, int d) {
+    const uint32_t lo = xor_lanes(static_cast<uint32_t>(v), d);
+    const uint32_t hi = xor_lanes(static_cast<uint32_t>(v >> 32), d);
+    return (static_cast<uint64_t>(hi) << 32) | lo;
+}
+
+// One compare-exchange of a bitonic network, seen from one element: e is the
+// element's index, d its partner's distance, s the size of the sequences
+// being merged.  Sequences whose index has bit s clear are sorted largest
+// first, so the final pass (s = n) leaves everything largest first.
+__device__ __forceinline__ uint64_t bitonic_keep(uint64_t mine, uint64_t other, int e, int d, int s) {
+    const bool lower = (e & d) == 0;
+    const bool desc = (e & s) == 0;
+    return (lower == desc) ? umax64(mine, other) : umin64(mine, other);
+}
+
+// Sorts the 64 NK keys of a wave, largest first: key[j] of lane l is element
+// j * 64 + l.  Steps with distance >= 64 stay in the lane's registers, the
+// others exchange with lane ^ d.
+template <int NK>
+__device__ __forceinline__ void wave_sort_desc(uint64_t (&key)[NK]) {
+    const int lane = threadIdx.x & (kWave - 1);
+    constexpr int n = kWave * NK;
+#pragma unroll
+    for (int s = 2; s <= n; s <<= 1) {
+#pragma unroll
+        for (int d = s >> 1; d > 0; d >>= 1) {
+            if (d >= kWave) {
+                const int dj = d / kWave;
+#pragma unroll
+                for (int j = 0; j < NK; ++j) {
+                    if ((j ^ dj) > j) {
+                        const uint64_t a = key[j], b = key[j ^ dj];
+                        key[j] = bitonic_keep(a, b, j * kWave, d, s);
+                        key[j ^ dj] = bitonic_keep(b, a, (j ^ dj) * kWave, d, s);
+                    }
+                }
+            } else {
+#pragma unroll
+                for (int j = 0; j < NK; ++j) key[j] = bitonic_keep(key[j], shfl_xor64(key[j], d), j * kWave + lane, d, s);
+            }
+        }
+    }
+}
+
+// Sorts NB * 1024 keys held by a 1024-thread workgroup, largest first:
+// key[j] of thread t is element j * 1024 + t.  Steps with distance < 64 are
+// shuffles inside a wave, steps with distance >= 1024 stay in registers, the
+// rest exchange through LDS (two buffers alternate, so one barrier a step).
+template <int NB>
+__device__ __forceinline__ void block_sort_desc(uint64_t (&key)[NB], uint64_t* lds /* 2 * NB * 1024 */) {
+    constexpr int T = kMergeThreads;
+    constexpr int n = T * NB;
+    const int t = threadIdx.x;
+    int buf = 0;
+#pragma unroll
+    for (int s = 2; s <= n; s <<= 1) {
+#pragma unroll
+        for (int d = s >> 1; d > 0; d >>= 1) {
+            if (d >= T) {
+                const int dj = d / T;
+#pragma unroll
+                for (int j = 0; j < NB; ++j) {
+                    if ((j ^ dj) > j) {
+                        const uint64_t a = key[j], b = key[j ^ dj];
+                        key[j] = bitonic_keep(a, b, j * T, d, s);
+                        key[j ^ dj] = bitonic_keep(b, a, (j ^ dj) * T, d, s);
+                    }
+                }
+            } else if (d >= kWave) {
+                uint64_t* B = lds + buf * (NB * T);
+#pragma unroll
+                for (int j = 0; j < NB; ++j) B[j * T + t] = key[j];
+                __syncthreads();
+#pragma unroll
+                for (int j = 0; j < NB; ++j) key[j] = bitonic_keep(key[j], B[j * T + (t ^ d)], j * T + t, d, s);
+                buf ^= 1;
+            } else {
+#pragma unroll
+                for (int j = 0; j < NB; ++j) key[j] = bitonic_keep(key[j], shfl_xor64(key[j], d), j * T + t, d, s);
+            }
+        }
+    }
+}
+
 // Largest of the NK keys below `bound` (0 if none), as a balanced tree.
 template <int NK>
 __device__ __forceinline__ uint64_t masked_max(const uint64_t (&key)[NK], uint64_t bound) {
@@ -133,7 +262,13 @@ void topk_chunk_kernel(const float* __restrict__ y, int64_t N, int k, int nwchun
         const int64_t idx = (static_cast<int64_t>(c) * KPL + i) * kWave + lane;
         key[i] = idx < N ? order_key(ym[idx], static_cast<uint32_t>(idx)) : 0ull;
     }
-    wave_select(key, k, cand + (static_cast<int64_t>(m) * nwchunks + c) * k);
+    uint64_t* out = cand + (static_cast<int64_t>(m) * nwchunks + c) * k;
+    if (KPL == 4 && k > kRoundsMaxK) {
+        wave_sort_desc(key);
+        if (lane < k) out[lane] = key[0];  // elements 0 .. k-1 of the sorted chunk
+    } else {
+        wave_select(key, k, out);
+    }
 }
 
 // Tournament over nlists <= 1024 sorted lists of k keys.
@@ -194,6 +329,108 @@ void topk_tournament_kernel(const float* __restrict__ y, int64_t N, int k, int n
         const float v = real ? y[static_cast<int64_t>(m) * N + idx] : __builtin_nanf("");
         top_idx[static_cast<int64_t>(m) * k + lane] = real ? static_cast<int32_t>(idx) : -1;
         top_val[static_cast<int64_t>(m) * k + lane] = softcap * tanhf(v / softcap);
+    }
+}
+
+// Stage 2 over nlists <= 1024 sorted lists of k keys (chunk: entries per
+// list's chunk, to find a key's list from its index).
+__global__ __launch_bounds__(kMergeThreads)
+void topk_select_kernel(const float* __restrict__ y, int64_t N, int k, int nlists, int chunk, float softcap,
+                        const uint64_t* __restrict__ cand, float* __restrict__ top_val,
+                        int32_t* __restrict__ top_idx) {
+    __shared__ uint64_t lds[2 * kMaxCand];  // sort buffers, then the candidates
+    __shared__ uint64_t sh_T;
+    __shared__ int sh_off[kWave + 1];
+    const int m = blockIdx.x;
+    const int t = threadIdx.x;
+    const int lane = t & (kWave - 1);
+    const uint64_t* cm = cand + static_cast<int64_t>(m) * nlists * k;
+
+    // 1. sort the heads; T = the k-th largest (0 if fewer than k lists)
+    uint64_t h[1] = {t < nlists ? cm[static_cast<int64_t>(t) * k] : 0ull};
+    block_sort_desc<1>(h, lds);
+    if (t == k - 1) sh_T = h[0];
+    __syncthreads();
+    const uint64_t T = sh_T;
+
+    // 2. thread t < k holds the t-th largest head; its list gives the keys
+    //    >= T, a prefix (lists are sorted).  The k lists are copied into LDS
+    //    with one round of loads, counted there, and their keys >= T packed
+    //    into the candidate buffer.
+    __shared__ int sh_list[kWave];
+    uint64_t* lists = lds;             // [k][k]
+    uint64_t* cbuf = lds + kMaxCand;   // [C]
+    if (t < k) {
+        sh_list[t] = h[0] != 0ull ? static_cast<int>((0xFFFFFFFFu - static_cast<uint32_t>(h[0])) /
+                                                     static_cast<uint32_t>(chunk))
+                                  : -1;
+    }
+    __syncthreads();
+    for (int e = t; e < k * k; e += kMergeThreads) {
+        const int o = e / k;
+        const int l = sh_list[o];
+        lists[e] = l >= 0 ? cm[static_cast<int64_t>(l) * k + (e - o * k)] : 0ull;
+    }
+    __syncthreads();
+    int cnt = 0;
+    if (t < k) {
+        for (int i = 0; i < k; ++i) {
+            const uint64_t v = lists[t * k + i];
+            cnt += (v >= T && v != 0ull) ? 1 : 0;
+        }
+    }
+    if (t < kWave) {
+        // exclusive prefix of the counts over wave 0 (k <= 64 lanes)
+        int inc = cnt;
+#pragma unroll
+        for (int o = 1; o < kWave; o <<= 1) {
+            const int v = __shfl_up(inc, o, kWave);
+            if (lane >= o) inc += v;
+        }
+        sh_off[lane + 1] = inc;
+        if (lane == 0) sh_off[0] = 0;
+    }
+    __syncthreads();
+    const int C = sh_off[kWave];  // <= k^2 <= kMaxCand
+    if (t < k) {
+        const int off = sh_off[t];
+        for (int i = 0; i < cnt; ++i) cbuf[off + i] = lists[t * k + i];
+    }
+    __syncthreads();
+
+    // 3. sort the C candidates; the first k are the result
+    uint64_t best = 0ull;  // thread r < k: the r-th largest key
+    if (C <= kWave) {
+        if (t < kWave) {
+            uint64_t key[1] = {lane < C ? cbuf[lane] : 0ull};
+            wave_sort_desc(key);
+            best = key[0];
+        }
+    } else if (C <= 4 * kWave) {
+        if (t < kWave) {
+            uint64_t key[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) key[j] = (j * kWave + lane < C) ? cbuf[j * kWave + lane] : 0ull;
+            wave_sort_desc(key);
+            best = key[0];
+        }
+    } else {
+        uint64_t key[kMaxCand / kMergeThreads];
+#pragma unroll
+        for (int j = 0; j < kMaxCand / kMergeThreads; ++j)
+            key[j] = (j * kMergeThreads + t < C) ? cbuf[j * kMergeThreads + t] : 0ull;
+        __syncthreads();  // the candidates are in registers: the buffers are free
+        block_sort_desc(key, lds);
+        best = key[0];
+    }
+    if (t < k) {
+        // k <= N guarantees a real key at every rank < k; a zero key would
+        // mean "nothing left" and is never dereferenced.
+        const uint32_t idx = 0xFFFFFFFFu - static_cast<uint32_t>(best);
+        const bool real = best != 0ull && idx < static_cast<uint64_t>(N);
+        const float v = real ? y[static_cast<int64_t>(m) * N + idx] : __builtin_nanf("");
+        top_idx[static_cast<int64_t>(m) * k + t] = real ? static_cast<int32_t>(idx) : -1;
+        top_val[static_cast<int64_t>(m) * k + t] = softcap * tanhf(v / softcap);
     }
 }
 
@@ -330,7 +567,10 @@ hipError_t launch_topk(const float* y, float* top_val, int32_t* top_idx, int64_t
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    if (nwchunks <= kMaxLists) {
+    if (nwchunks <= kMaxLists && k > kRoundsMaxK) {
+        hipLaunchKernelGGL(topk_select_kernel, dim3(static_cast<unsigned>(M)), dim3(kMergeThreads), 0, stream,
+                           y, N, k, nwchunks, kWave * keys_per_lane(N), softcap, cand, top_val, top_idx);
+    } else if (nwchunks <= kMaxLists) {
         hipLaunchKernelGGL(topk_tournament_kernel, dim3(static_cast<unsigned>(M)), dim3(kMergeThreads), 0, stream,
                            y, N, k, nwchunks, softcap, cand, top_val, top_idx);
     } else {

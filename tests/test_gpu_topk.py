@@ -142,7 +142,11 @@ def _topk_f32(y, k):
 
 # Row lengths around the stage-1 chunk-size steps (4, 16 and 64 keys per lane)
 # and past 1024 chunks of 4096 (the rescanning merge).
-@pytest.mark.parametrize("N,k", [(262144, 10), (262145, 64), (1048576, 7), (1048577, 10), (4194305, 10)])
+# k <= 16 takes the round-based selection, larger k the sorted chunks and
+# the threshold stage 2 (with 4 keys per lane up to 262,144 entries, with
+# rounds in stage 1 beyond).
+@pytest.mark.parametrize("N,k", [(262144, 10), (262144, 40), (262144, 17), (262145, 64), (1048576, 7),
+                                 (1048577, 10), (1048576, 40), (4194305, 10)])
 def test_topk_long_rows(N, k):
     say(f"qmvdbg_topk_f32 N={N} k={k}")
     rng = np.random.default_rng(N % 1000 + k)
@@ -156,11 +160,11 @@ def test_topk_long_rows(N, k):
         assert np.all(np.abs(vals[m] - zr) <= 1e-5)
 
 
-@pytest.mark.parametrize("N", [5000, 300000, 2000000])
-def test_topk_one_chunk_holds_every_winner(N):
+@pytest.mark.parametrize("N,k", [(5000, 64), (300000, 64), (2000000, 64), (5000, 16), (262144, 40)])
+def test_topk_one_chunk_holds_every_winner(N, k):
     # A decreasing row puts the k largest values in the first chunk, so one
     # list of the merge supplies every winner (more than it keeps in registers).
-    say(f"qmvdbg_topk_f32 decreasing row N={N}")
+    say(f"qmvdbg_topk_f32 decreasing row N={N} k={k}")
     y = (np.arange(N, 0, -1, dtype=np.float64) * 1e-3).astype(np.float32)[None, :]
-    vals, idx = _topk_f32(y, 64)
-    assert idx[0].tolist() == oracle.topk(y[0].astype(np.float64), 64).tolist()
+    vals, idx = _topk_f32(y, k)
+    assert idx[0].tolist() == oracle.topk(y[0].astype(np.float64), k).tolist()
