@@ -105,8 +105,8 @@ def main():
         copy_calibration(args.copy_calibration)
         return
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the path has no multi-GPU part "
-              "in this build", file=sys.stderr)
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): the path has no multi-GPU part",
+              file=sys.stderr)
         sys.exit(2)
 
     import torch

@@ -276,9 +276,9 @@ __global__ __launch_bounds__(kMergeThreads)
 void topk_tournament_kernel(const float* __restrict__ y, int64_t N, int k, int nlists, float softcap,
                             const uint64_t* __restrict__ cand, float* __restrict__ top_val,
                             int32_t* __restrict__ top_idx) {
-    // Round 1: every wave runs its own tournament over its 64 lists (a wave
+    // Level 1: every wave runs its own tournament over its 64 lists (a wave
     // maximum per round, no workgroup barrier) and keeps its k winners in
-    // LDS.  Round 2: wave 0 runs the tournament over the 16 waves' lists.
+    // LDS.  Level 2: wave 0 runs the tournament over the 16 waves' lists.
     __shared__ uint64_t wlist[kMergeWaves][64];
     const int m = blockIdx.x;
     const int t = threadIdx.x;
