@@ -43,8 +43,8 @@
  *   dispatch, not assumed; a path may not silently drop work; captable
  *   findings F6, F13 and F17 are the defects this rules out]:
  *     QMV_ERR_NULL       a required pointer is NULL
- *     QMV_ERR_SHAPE      N, M < 1; K < 32 or K % 32 != 0 (K % 256 != 0 for
- *                        Q4_K, Q6_K); a size or a byte count overflows int64, or
+ *     QMV_ERR_SHAPE      N, M < 1; M > 65535; K < 32 or K % 32 != 0 (K % 256
+ *                        != 0 for Q4_K, Q6_K); a size or a byte count overflows int64, or
  *                        N >= 2^31
  *     QMV_ERR_ALIGN      W or a workspace is not 16-byte aligned, or an f32
  *                        / int32 buffer is not 4-byte aligned

@@ -14,6 +14,9 @@
 namespace {
 
 constexpr int64_t kMaxN = (int64_t{1} << 31) - 1;
+// Activation rows: the matrix-vector entry points launch once per row, so a
+// bound keeps a mistaken M from queueing an unbounded number of launches.
+constexpr int64_t kMaxM = 65535;
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
@@ -28,7 +31,7 @@ bool mul_ok(int64_t a, int64_t b, int64_t* out) {
 // activations.  elems is the weights per block (32, or 256 for Q4_K) and
 // bytes the bytes per block.
 int check_shape(int64_t N, int64_t K, int64_t M, int64_t elems, int64_t bytes) {
-    if (N < 1 || M < 1 || K < 32) return QMV_ERR_SHAPE;
+    if (N < 1 || M < 1 || K < 32 || M > kMaxM) return QMV_ERR_SHAPE;
     if (K % 32 != 0 || K % elems != 0) return QMV_ERR_SHAPE;
     if (N > kMaxN || K > kMaxN) return QMV_ERR_SHAPE;
     int64_t t;
@@ -68,7 +71,7 @@ const char* qmv_status_str(int status) {
     switch (status) {
     case QMV_OK: return "ok";
     case QMV_ERR_NULL: return "null pointer";
-    case QMV_ERR_SHAPE: return "invalid shape (N, M >= 1; K >= 32, K % 32 == 0, K % 256 == 0 for Q4_K and Q6_K; no overflow)";
+    case QMV_ERR_SHAPE: return "invalid shape (N >= 1; 1 <= M <= 65535; K >= 32, K % 32 == 0, K % 256 == 0 for Q4_K and Q6_K; no overflow)";
     case QMV_ERR_ALIGN: return "misaligned buffer (W and workspace 16 B, float/int32 buffers 4 B)";
     case QMV_ERR_WORKSPACE: return "workspace too small";
     case QMV_ERR_LAUNCH: return "kernel launch failed";

@@ -71,6 +71,7 @@ def test_gemv_validation(name):
     assert call(name, FAKE, FAKE, FAKE, 8, 33 * 32 + 1, 1, S) == SHAPE
     assert call(name, FAKE, FAKE, FAKE, 1 << 31, 256, 1, S) == SHAPE
     assert call(name, FAKE, FAKE, FAKE, 8, 1 << 21, 1 << 41, S) == SHAPE  # M*K*4 overflows int64
+    assert call(name, FAKE, FAKE, FAKE, 1, 256, 65536, S) == SHAPE      # activation rows are bounded
     assert call(name, FAKE + 8, FAKE, FAKE, 8, 256, 1, S) == ALIGN
     assert call(name, FAKE, FAKE + 2, FAKE, 8, 256, 1, S) == ALIGN
     assert call(name, FAKE, FAKE, FAKE + 1, 8, 256, 1, S) == ALIGN
