@@ -541,74 +541,104 @@ void gemv_qkv_kernel(const uint8_t* __restrict__ Wq, const uint8_t* __restrict__
 
 // ----------------------------------------------------------- split kernel
 // K % 256 == 0 and G = K/256 > 63: rows longer than a wave has lanes for one
-// unit each (the FFN down projection, K = 21504, has G = 84).  A workgroup
-// of RG x KS waves stages all of x once (up to 160 KB of LDS); wave (rg, kq)
-// takes K-slice kq -- units [kq*Gs, kq*Gs + Gs) -- of S rows, one unit per
-// lane as in the unit kernel.  The KS slice sums of a row meet in LDS and
-// are added in slice order, so the result does not depend on timing.
+// unit each (the FFN down projection, K = 21504, has G = 84).  Each row is
+// cut into KS slices of Gs units; a "slot" is S rows x one slice, one unit
+// per lane, exactly like a pass of the unit kernel on a short row.
+//   * A workgroup stages all of x once (up to 160 KB of LDS) and owns a
+//     contiguous range of row groups (S rows each); the ranges differ by at
+//     most one group, so every CU streams the same number of bytes.
+//   * Its waves take the range's slots in turn (slot = group * KS + slice)
+//     with no barrier between slots; each wave requests its next slot's
+//     weights as soon as the current ones are decoded.
+//   * Slice sums go to LDS.  After one barrier per chunk of CH groups, the
+//     KS slice sums of each row are added in slice order, so the result does
+//     not depend on timing.
 constexpr int kSplitThreads = 1024;
 
 template <int F, bool GIN>
 __global__ __launch_bounds__(kSplitThreads)
 void gemv_split_kernel(const uint8_t* __restrict__ W, const uint8_t* __restrict__ Ws, const float* __restrict__ x,
                        const float* __restrict__ xu, float* __restrict__ y, int N, int G, int KS, int Gs, int S,
-                       int RG, int npasses) {
+                       int NG, int CH) {
     constexpr int UB = UnitInfo<F>::kBytes;
     extern __shared__ float xs[];
-    float* red = xs + G * kXsStride;  // [2][RG][S][KS] slice sums, double-buffered by pass
+    float* red = xs + G * kXsStride;  // [CH][S][KS] slice sums of the current chunk
 
+    const int nwaves = blockDim.x / kWave;
     const int wave = threadIdx.x / kWave;
     const int lane = threadIdx.x & (kWave - 1);
-    const int rg = wave / KS;
-    const int kq = wave - rg * KS;
     const int seg = lane / Gs;
     const int uu = lane - seg * Gs;
-    const int u = kq * Gs + uu;
-    const bool live = seg < S && u < G;
-    const int uc = u < G ? u : G - 1;  // lanes past the last unit load a valid one, summed as 0
     const int64_t row_bytes = static_cast<int64_t>(G) * UB;
+
+    // this workgroup's row groups [g0, g1)
+    const int base = NG / static_cast<int>(gridDim.x);
+    const int rem = NG - base * static_cast<int>(gridDim.x);
+    const int b = blockIdx.x;
+    const int g0 = b * base + (b < rem ? b : rem);
+    const int g1 = g0 + base + (b < rem ? 1 : 0);
 
     uint32_t U[1][kUnitWords<F>];
     uint32_t sh[1];
-    auto load = [&](int p) {
-        int row = (p * RG + rg) * S + seg;
-        row = row < N ? row : N - 1;
+    // slot index within the chunk starting at group c0 -> (row, unit)
+    auto load = [&](int c0, int slot) {
+        const int g = c0 + slot / KS;
+        const int u = (slot % KS) * Gs + uu;
+        const int uc = u < G ? u : G - 1;  // lanes past the last unit load a valid one, summed as 0
+        int row = g * S + seg;
+        row = row < N ? row : N - 1;  // rows past the end load the last row; never stored
         load_unit<F>(U[0], sh[0], W + row * row_bytes + uc * UB,
                      Ws + (static_cast<int64_t>(row) * G + uc) * kUnitScaleBytes<F>);
     };
 
-    int pass = blockIdx.x;
-    if (pass < npasses) load(pass);
-    stage_x<GIN>(xs, x, xu, G, RG * KS * kWave);  // the launch's block size
+    int c0 = g0;
+    int cn = min(CH, g1 - c0);
+    int slot = wave;
+    bool have = false;  // U holds the weights of (c0, slot)
+    if (slot < cn * KS) {
+        load(c0, slot);
+        have = true;
+    }
+    stage_x<GIN>(xs, x, xu, G, blockDim.x);
     __syncthreads();
 
-    int buf = 0;
-    while (pass < npasses) {
-        int xoff = uc * kXsStride;
-        asm volatile("" : "+v"(xoff));
-        float acc[1];
-        dot_units<F, 1>(U, sh, xs + xoff, acc);
-        // The weights of this pass are consumed: start the next pass's loads
-        // before the barrier, so that HBM is not idle while the workgroup
-        // waits for its slowest wave.
-        const int next = pass + gridDim.x;
-        if (next < npasses) load(next);
-        const float v = segment_sum(live ? acc[0] : 0.f, uu, Gs);
-        if (seg < S && uu == 0) red[((buf * RG + rg) * S + seg) * KS + kq] = v;
+    while (c0 < g1) {
+        const int cn_next_c0 = c0 + cn;
+        const int cn_next = min(CH, g1 - cn_next_c0);
+        // a wave with no slot in the previous chunk has not loaded yet
+        if (!have && slot < cn * KS) load(c0, slot);
+        while (slot < cn * KS) {
+            const int kq = slot % KS;
+            const int u = kq * Gs + uu;
+            const bool live = seg < S && u < G;
+            int xoff = (u < G ? u : G - 1) * kXsStride;
+            asm volatile("" : "+v"(xoff));
+            float acc[1];
+            dot_units<F, 1>(U, sh, xs + xoff, acc);
+            const int gl = slot / KS;
+            // The weights of this slot are consumed: request the next slot's
+            // (in this chunk or, past its end, in the next one).
+            const int next = slot + nwaves;
+            have = true;
+            if (next < cn * KS) load(c0, next);
+            else if (wave < cn_next * KS) load(cn_next_c0, wave);
+            else have = false;
+            const float v = segment_sum(live ? acc[0] : 0.f, uu, Gs);
+            if (seg < S && uu == 0) red[(gl * S + seg) * KS + kq] = v;
+            slot = next;
+        }
         __syncthreads();
-        if (static_cast<int>(threadIdx.x) < RG * S) {
-            const int r = threadIdx.x;
-            const int row = pass * RG * S + r;
-            const float* part = red + (buf * RG * S + r) * KS;
+        for (int r = threadIdx.x; r < cn * S; r += blockDim.x) {
+            const int row = c0 * S + r;
+            const float* part = red + r * KS;
             float t = part[0];
             for (int q = 1; q < KS; ++q) t += part[q];
             if (row < N) y[row] = t * kRowScale<F>;
         }
-        // The next pass writes the other buffer; this one is rewritten only
-        // after the next pass's barrier, which every reader above passes
-        // after its reads.
-        buf ^= 1;
-        pass = next;
+        __syncthreads();  // the sums are read before the next chunk rewrites them
+        c0 = cn_next_c0;
+        cn = cn_next;
+        slot = wave;
     }
 }
 
@@ -748,14 +778,15 @@ hipError_t launch_unit(const void* W0, const void* W1, const float* x, const flo
 }
 
 // Slicing of a long row for gemv_split_kernel: KS slices of Gs units, S rows
-// per wave, RG row groups per workgroup.
+// per slot, NG row groups over `blocks` workgroups of `threads`, CH groups
+// per chunk of slice sums in LDS.
 struct SplitPlan {
-    int KS, Gs, S, RG, npasses, blocks;
+    int KS, Gs, S, NG, CH, blocks, threads;
     size_t lds;
 };
 
 // Picks the slice count that keeps the most lanes on real units (ties: fewer
-// slices), up to 16 waves per workgroup.  False if x does not fit in LDS.
+// slices).  False if x does not fit in LDS.
 bool plan_split(int G, int N, SplitPlan* p) {
     int best = 0;
     double best_eff = -1.0;
@@ -773,26 +804,31 @@ bool plan_split(int G, int N, SplitPlan* p) {
     p->KS = best;
     p->Gs = (G + best - 1) / best;
     p->S = kWave / p->Gs;
-    p->RG = (kSplitThreads / kWave) / best;
-    p->lds = (static_cast<size_t>(G) * kXsStride + 2 * static_cast<size_t>(p->RG) * p->S * p->KS) * sizeof(float);
+    p->NG = (N + p->S - 1) / p->S;
     const size_t max_lds = static_cast<size_t>(device_max_lds());
-    if (p->lds > max_lds) return false;
-    const int rows_per_pass = p->RG * p->S;
-    p->npasses = (N + rows_per_pass - 1) / rows_per_pass;
-    // Resident workgroups per CU: by LDS, and at most two of 16 waves.
-    int per_cu = static_cast<int>(max_lds / p->lds);
-    per_cu = per_cu < 1 ? 1 : (per_cu > 2 ? 2 : per_cu);
+    const size_t x_bytes = static_cast<size_t>(G) * kXsStride * sizeof(float);
+    const size_t group_bytes = static_cast<size_t>(p->S) * p->KS * sizeof(float);
+    if (x_bytes + group_bytes > max_lds) return false;
+    // Two workgroups of 8 waves per CU when both fit in LDS with a chunk of
+    // at least 8 groups each, else one of 16 waves.
+    const int per_cu = (2 * (x_bytes + 8 * group_bytes) <= max_lds) ? 2 : 1;
+    p->threads = kSplitThreads / per_cu;
     const int max_blocks = device_cus() * per_cu;
-    p->blocks = p->npasses < max_blocks ? p->npasses : max_blocks;
+    p->blocks = p->NG < max_blocks ? p->NG : max_blocks;
+    const int per_block = (p->NG + p->blocks - 1) / p->blocks;
+    const size_t room = (max_lds / per_cu - x_bytes) / group_bytes;
+    p->CH = static_cast<int>(room < static_cast<size_t>(per_block) ? room : static_cast<size_t>(per_block));
+    if (p->CH > 1024) p->CH = 1024;
+    p->lds = x_bytes + static_cast<size_t>(p->CH) * group_bytes;
     return true;
 }
 
 template <int F, bool GIN>
 hipError_t launch_split(const void* W, const void* Ws, const float* x, const float* xu, float* y, int N, int G,
                         const SplitPlan& p, hipStream_t stream) {
-    hipLaunchKernelGGL((gemv_split_kernel<F, GIN>), dim3(p.blocks), dim3(p.RG * p.KS * kWave), p.lds, stream,
+    hipLaunchKernelGGL((gemv_split_kernel<F, GIN>), dim3(p.blocks), dim3(p.threads), p.lds, stream,
                        static_cast<const uint8_t*>(W), static_cast<const uint8_t*>(Ws), x, xu, y, N, G, p.KS, p.Gs,
-                       p.S, p.RG, p.npasses);
+                       p.S, p.NG, p.CH);
     return hipGetLastError();
 }
 
