@@ -190,6 +190,9 @@ def main():
         "traffic_source": TRAFFIC_PROFILE if dom["hbm_traffic_bytes"] is not None else None,
     }
 
+    ceiling = read_ceiling(torch, qmv, dev, {"single": wbytes, "pair": 2 * wbytes})
+    roofline["frac_of_read_ceiling"] = round(dom["GB/s"] / ceiling["pair"]["GB/s"], 4)
+
     rows = None
     if not args.no_rows:
         rows = measure_rows(torch, qmv, synth, dev)
@@ -220,11 +223,34 @@ def main():
         "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),
         "wall_s_timed": round(wall, 4),
         "roofline": roofline,
+        "read_ceiling": ceiling,
         "kernels": kernels,
         "cpu_baseline": cpu,
         "rows": rows,
     }
     print(json.dumps(out))
+
+
+def read_ceiling(torch, qmv, dev, sizes, iters=50):
+    """The plain streaming-read rate (qmvdbg_stream_read: every byte loaded once
+    with coalesced 16-byte loads) at the byte counts of the timed launches,
+    over rotating buffers that add up to about 1 GB (4x the last-level cache)
+    so that every read comes from HBM; the best of several grids."""
+    out = {}
+    word = torch.zeros(16384, dtype=torch.int32, device=dev)
+    for name, nbytes in sizes.items():
+        nbytes -= nbytes % 16
+        copies = max(4, -(-1_000_000_000 // nbytes))
+        bufs = [torch.full((nbytes,), i + 1, dtype=torch.uint8, device=dev) for i in range(copies)]
+        best = None
+        for wg in (2048, 4096, 8192, 16384):
+            ms = _time_loop(torch, lambda i: qmv.qmvdbg_stream_read(bufs[i % copies], nbytes, word, wg), iters)
+            if best is None or ms < best[0]:
+                best = (ms, wg)
+        out[name] = {"bytes": nbytes, "copies": copies, "us": round(best[0] * 1e3, 2), "workgroups": best[1],
+                     "GB/s": round(nbytes / (best[0] * 1e-3) / 1e9, 1)}
+        del bufs
+    return out
 
 
 def _time_loop(torch, fn, iters, warm=5):

@@ -265,6 +265,19 @@ int qmvdbg_sample_f32(const float* top_val, const int32_t* top_idx, const float*
                       int32_t* token, int32_t* nucleus, int64_t M, int32_t k,
                       float temperature, float top_p, hipStream_t stream);
 
+/* A plain streaming read, the measured ceiling for the kernels above: reads
+ * the `bytes` bytes at p (a multiple of 16, p 16-byte aligned) once with
+ * coalesced 16-byte loads, on a grid of `workgroups` 256-thread workgroups.
+ * out[w], w < workgroups, receives the XOR of the 32-bit words that
+ * workgroup w read (0 if none), so the XOR of out[0 .. workgroups) is the
+ * XOR of the whole buffer.  out must hold `workgroups` words.
+ * Errors: NULL pointers -> QMV_ERR_NULL; bytes < 16 or not a multiple of
+ * 16 -> QMV_ERR_SHAPE; workgroups outside [1, 65536] -> QMV_ERR_ARG;
+ * misaligned p or out -> QMV_ERR_ALIGN.
+ * [roadmap K5: the tied output projection is judged against the
+ *  sustainable memory-streaming rate, which this read measures on MI355X] */
+int qmvdbg_stream_read(const void* p, int64_t bytes, uint32_t* out, int32_t workgroups, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -288,4 +288,12 @@ int qmvdbg_sample_f32(const float* top_val, const int32_t* top_idx, const float*
     return launched(qmv::launch_sample(top_val, top_idx, u, token, nucleus, M, k, temperature, top_p, stream));
 }
 
+int qmvdbg_stream_read(const void* p, int64_t bytes, uint32_t* out, int32_t workgroups, hipStream_t stream) {
+    if (!p || !out) return QMV_ERR_NULL;
+    if (bytes < 16 || bytes % 16 != 0) return QMV_ERR_SHAPE;
+    if (workgroups < 1 || workgroups > 65536) return QMV_ERR_ARG;
+    if (!aligned(p, 16) || !aligned(out, 4)) return QMV_ERR_ALIGN;
+    return launched(qmv::launch_stream_read(p, bytes, out, workgroups, stream));
+}
+
 }  // extern "C"

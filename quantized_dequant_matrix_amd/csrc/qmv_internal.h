@@ -58,6 +58,7 @@ hipError_t launch_q4_0_q8_blocksums(const void* W, const int8_t* qx, int32_t* is
 // Q4_0 x float32 activations (small M).  The workspace layout (and size)
 // depends on (N, K, M) only.
 size_t qmm_f32act_ws_bytes(int64_t N, int64_t K, int64_t M);
+hipError_t launch_stream_read(const void* p, int64_t bytes, uint32_t* out, int workgroups, hipStream_t stream);
 hipError_t launch_qmm_f32act(const void* W, const float* x, float* y, int64_t N, int64_t K, int64_t M,
                              void* ws, hipStream_t stream);
 

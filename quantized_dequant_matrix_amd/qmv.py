@@ -48,6 +48,7 @@ _SIGS = {
     "qmvdbg_q4_0_q8_blocksums": ([_P, _P, _P, _I64, _I64, _I64, _P], ctypes.c_int),
     "qmvdbg_topk_f32": ([_P, _P, _P, _I64, _I64, _I32, _F, _P, _SZ, _P], ctypes.c_int),
     "qmvdbg_sample_f32": ([_P, _P, _P, _P, _P, _I64, _I32, _F, _F, _P], ctypes.c_int),
+    "qmvdbg_stream_read": ([_P, _I64, _P, _I32, _P], ctypes.c_int),
 }
 for _name, (_args, _res) in _SIGS.items():
     _fn = getattr(lib, _name)
@@ -179,3 +180,7 @@ def logits_sample(W_q8_0, x, u, token, nucleus, top_val, top_idx, N, K, M, k, so
 def qmvdbg_sample_f32(top_val, top_idx, u, token, nucleus, M, k, temperature, top_p, stream=None):
     _call("qmvdbg_sample_f32", _ptr(top_val), _ptr(top_idx), _ptr(u), _ptr(token), _ptr(nucleus), M, k,
           temperature, top_p, _stream(stream))
+
+
+def qmvdbg_stream_read(p, nbytes, out, workgroups, stream=None):
+    _call("qmvdbg_stream_read", _ptr(p), nbytes, _ptr(out), workgroups, _stream(stream))

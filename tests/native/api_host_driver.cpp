@@ -41,6 +41,8 @@ hipError_t launch_q4_0_q8_blocksums(const void*, const int8_t*, int32_t*, int64_
 size_t qmm_f32act_ws_bytes(int64_t N, int64_t K, int64_t M) { return static_cast<size_t>(M * K * 4 + N * M * 4 + 256); }
 hipError_t launch_qmm_f32act(const void*, const float*, float*, int64_t N, int64_t K, int64_t, void*, hipStream_t) {
     rec(N, K); return hipSuccess; }
+hipError_t launch_stream_read(const void*, int64_t bytes, uint32_t*, int workgroups, hipStream_t) {
+    rec(bytes, workgroups); return hipSuccess; }
 }  // namespace qmv
 
 static int failures = 0;
@@ -106,6 +108,12 @@ int main() {
            QMV_OK);
     EXPECT(qmvdbg_sample_f32(y, idx, u, idx + 8, idx + 16, 2, 10, 0.7f, 0.9f, s), QMV_OK);
     EXPECT(qmvdbg_quantize_q8(x, reinterpret_cast<int8_t*>(ws), y, 256, 2, s), QMV_OK);
+    g_calls = 0;
+    EXPECT(qmvdbg_stream_read(W, 4096, reinterpret_cast<uint32_t*>(idx), 7, s), QMV_OK);
+    if (g_calls != 1 || g_N != 4096 || g_K != 7) { std::fprintf(stderr, "stream read launch\n"); ++failures; }
+    EXPECT(qmvdbg_stream_read(W, big & ~int64_t{15}, reinterpret_cast<uint32_t*>(idx), 1, s), QMV_OK);
+    EXPECT(qmvdbg_stream_read(W, 4096, reinterpret_cast<uint32_t*>(idx), 0, s), QMV_ERR_ARG);
+    EXPECT(qmvdbg_stream_read(W, 4095, reinterpret_cast<uint32_t*>(idx), 0, s), QMV_ERR_SHAPE);
     for (int st = -1; st < 9; ++st) (void)qmv_status_str(st);
 
     if (failures) { std::fprintf(stderr, "%d failures\n", failures); return 1; }

@@ -26,7 +26,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported_and_bound():
     names = declared_functions()
-    assert "qmv_q4_0" in names and "logits_topk" in names and len(names) == 22
+    assert "qmv_q4_0" in names and "logits_topk" in names and len(names) == 23
     for n in names:
         assert hasattr(qmv.lib, n), n
     assert sorted(qmv.EXPORTS) == names
@@ -232,3 +232,14 @@ def test_debug_entry_validation():
     assert call("qmvdbg_quantize_q8", None, FAKE, FAKE, 64, 1, S) == NUL
     assert call("qmvdbg_q4_0_q8_blocksums", FAKE, FAKE + 4, FAKE, 8, 64, 1, S) == ALIGN
     assert call("qmvdbg_topk_f32", FAKE, FAKE, FAKE, 100, 1, 101, 30.0, FAKE, 1 << 20, S) == ARG
+
+
+def test_stream_read_validation():
+    assert call("qmvdbg_stream_read", None, 4096, FAKE, 8, S) == NUL
+    assert call("qmvdbg_stream_read", FAKE, 4096, None, 8, S) == NUL
+    assert call("qmvdbg_stream_read", FAKE, 0, FAKE, 8, S) == SHAPE
+    assert call("qmvdbg_stream_read", FAKE, 4100, FAKE, 8, S) == SHAPE
+    assert call("qmvdbg_stream_read", FAKE, 4096, FAKE, 0, S) == ARG
+    assert call("qmvdbg_stream_read", FAKE, 4096, FAKE, 65537, S) == ARG
+    assert call("qmvdbg_stream_read", FAKE + 8, 4096, FAKE, 8, S) == ALIGN
+    assert call("qmvdbg_stream_read", FAKE, 4096, FAKE + 2, 8, S) == ALIGN
