@@ -38,13 +38,13 @@ TRAFFIC_PROFILE = os.path.join("profiles", "qmv_bench_workloads_hbm_traffic.md")
 # kernel symbol of each timed launch, and its workgroups per CU at most
 KERNEL_OF = {
     "qmv_q4_0": ("qmv::gemv_unit_kernel<0, 1, false, false>", 3),
-    "qmv_q4_0_geglu": ("qmv::gemv_unit_kernel<0, 1, true, false>", 4),
+    "qmv_q4_0_geglu": ("qmv::gemv_unit_kernel<0, 1, true, false>", 8),
 }
 
 
 def unit_grid(N: int, K: int, cus: int, per_cu: int) -> int:
     """Workgroups of the unit GEMV launch: 4 waves per workgroup, one pass of
-    64 // (K/256) rows per wave, capped at the resident count."""
+    64 // (K/256) rows per wave, capped at per_cu workgroups per CU."""
     rows_per_pass = 64 // (K // 256)
     npasses = -(-N // rows_per_pass)
     return min(-(-npasses // 4), cus * per_cu)

@@ -763,11 +763,13 @@ hipError_t launch_unit(const void* W0, const void* W1, const float* x, const flo
     const int S = kWave / G;
     const int rows_per_pass = S * R;
     const int npasses = (N + rows_per_pass - 1) / rows_per_pass;
-    // At most as many workgroups as are resident at once (4 per CU at
-    // <= 128 VGPRs); longer matrices take several passes per wave.  One
-    // matrix at a time runs best with 3 per CU: a wave's first loads then
-    // share the memory system with fewer others and arrive sooner.
-    const int max_blocks = device_cus() * (PAIR ? 4 : 3);
+    // One matrix at a time runs best with 3 workgroups per CU, all resident
+    // at once, its waves taking several passes each: a wave's first loads
+    // then share the memory system with fewer others and arrive sooner.  The
+    // pair (4 resident per CU at its 123 VGPRs) runs best with one pass per
+    // wave and workgroups replacing each other as they finish (1792 at the
+    // gate shape), up to 8 per CU before waves loop.
+    const int max_blocks = device_cus() * (PAIR ? 8 : 3);
     int blocks = (npasses + kWavesPerBlock - 1) / kWavesPerBlock;
     if (blocks > max_blocks) blocks = max_blocks;
     const size_t lds = static_cast<size_t>(G) * kXsStride * sizeof(float);
