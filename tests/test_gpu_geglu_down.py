@@ -43,7 +43,8 @@ def check(fmt, W, g, u, N, K, M, what):
 
 
 # unit kernel (K <= 16128), split kernel (longer K), generic kernel (K % 256 != 0, Q4_0 only)
-SHAPES = [(1, 256), (65, 5376), (7, 96), (13, 5408), (29, 21504), (12, 16640)]
+# (9001, 40192): the split kernel's range in two chunks (see test_gpu_gemv)
+SHAPES = [(1, 256), (65, 5376), (7, 96), (13, 5408), (29, 21504), (12, 16640), (9001, 40192)]
 
 
 @pytest.mark.parametrize("fmt", FMTS)

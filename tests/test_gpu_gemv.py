@@ -118,6 +118,21 @@ def test_long_rows(fmt, N, K):
     assert_within(y, yr, oracle.float_tol(S), f"qmv_{fmt} {N}x{K}")
 
 
+# More row groups per workgroup than its LDS holds slice sums for: at
+# K = 40192 the activations fill 163 KB of LDS, room is left for 14 groups of
+# 2 rows, and 9001 rows give each of the 256 workgroups 17 or 18 groups, so
+# the split kernel takes its range in two chunks (the second partial) and the
+# last group has one row.
+@pytest.mark.parametrize("fmt", FMTS)
+def test_long_rows_chunked(fmt):
+    N, K = 9001, 40192
+    say(f"qmv_{fmt} split kernel in chunks N={N} K={K}")
+    W, x = synth.problem(fmt, N, K, 1, 4242)
+    y = run_gemv(fmt, W, x, N, K)
+    yr, S = oracle.qmv(fmt, W, N, K, x)
+    assert_within(y, yr, oracle.float_tol(S), f"qmv_{fmt} {N}x{K}")
+
+
 @pytest.mark.parametrize("name,fmt", [("c4", "q4_0"), ("q4k_down", "q4_k"), ("q6k_down", "q6_k")])
 def test_down_shape_full(name, fmt):
     c = synth.CONFIGS[name]

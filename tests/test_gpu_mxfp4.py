@@ -27,7 +27,7 @@ def run(codes, scales, x, N, K, M=1):
 # unit kernel (K % 256 == 0, K <= 16128), split kernel (longer K), generic
 # kernel (K % 256 != 0, and K > 40192)
 SHAPES = [(1, 32), (5, 64), (7, 96), (64, 256), (65, 256), (3, 768), (33, 4096), (129, 5376), (17, 16128),
-          (9, 16384), (8, 16640), (13, 5408), (29, 21504), (12, 21504), (5, 40960)]
+          (9, 16384), (8, 16640), (13, 5408), (29, 21504), (12, 21504), (5, 40960), (9001, 40192)]
 
 
 @pytest.mark.parametrize("N,K", SHAPES)
