@@ -240,7 +240,7 @@ def read_ceiling(torch, qmv, dev, sizes, iters=50):
     word = torch.zeros(16384, dtype=torch.int32, device=dev)
     for name, nbytes in sizes.items():
         nbytes -= nbytes % 16
-        copies = max(4, -(-1_000_000_000 // nbytes))
+        copies = max(2 if nbytes >= 500_000_000 else 4, -(-1_000_000_000 // nbytes))
         bufs = [torch.full((nbytes,), i + 1, dtype=torch.uint8, device=dev) for i in range(copies)]
         best = None
         for wg in (2048, 4096, 8192, 16384):
@@ -408,6 +408,7 @@ def measure_rows(torch, qmv, synth, dev):
     y = torch.empty((1, c["N"]), device=dev)
     ms = _time_loop(torch, lambda i: qmv.qmv_q8_0(Wd, xd, y, c["N"], c["K"], 1), 20, warm=3)
     res["c3_qmv_q8_0_only_262144x5376"] = {"us": ms * 1e3, "bytes": b, "GB/s": b / ms / 1e6}
+    c3_weight_bytes = Wd.numel()
     # token selection on the device: top-40, then a top-p draw (0.95, T = 1)
     k40 = 40
     wsb40 = qmv.logits_topk_ws_bytes(c["N"], 1, k40)
@@ -426,17 +427,25 @@ def measure_rows(torch, qmv, synth, dev):
                     warm=3)
     res["c3_topk_only_262144_k10"] = {"us": ms * 1e3, "bytes": c["N"] * 4, "GB/s": c["N"] * 4 / ms / 1e6}
     del Wd
-    # the 1024-wide drafter projection over the same vocabulary (Q8_0 262144 x 1024) + selection
+    # the 1024-wide drafter projection over the same vocabulary (Q8_0 262144 x 1024) + selection; four
+    # rotating copies (1.1 GB, 4x the last-level cache), so that the weights come from HBM
     Kd = 1024
-    Wm = t(synth.q8_0_weights(c["N"], Kd, 1103))
+    Wm = [t(synth.q8_0_weights(c["N"], Kd, 1103))]
+    Wm += [Wm[0].clone() for _ in range(3)]
     xm = t(synth.activations(1, Kd, 1104))
-    ms = _time_loop(torch, lambda i: qmv.logits_sample(Wm, xm, ud, tok, nuc, v40, i40, c["N"], Kd, 1, k40,
+    ms = _time_loop(torch, lambda i: qmv.logits_sample(Wm[i % 4], xm, ud, tok, nuc, v40, i40, c["N"], Kd, 1, k40,
                                                        c["softcap"], 1.0, 0.95, ws40, wsb40), 50, warm=3)
-    bm = Wm.numel() + Kd * 4 + c["N"] * 4
+    bm = Wm[0].numel() + Kd * 4 + c["N"] * 4
     res["mtp_logits_sample_q8_0_262144x1024_k40_p0.95"] = {"us": ms * 1e3, "bytes": bm, "GB/s": bm / ms / 1e6}
-    ms = _time_loop(torch, lambda i: qmv.qmv_q8_0(Wm, xm, y, c["N"], Kd, 1), 50, warm=3)
+    ms = _time_loop(torch, lambda i: qmv.qmv_q8_0(Wm[i % 4], xm, y, c["N"], Kd, 1), 50, warm=3)
     res["mtp_qmv_q8_0_only_262144x1024"] = {"us": ms * 1e3, "bytes": bm, "GB/s": bm / ms / 1e6}
+    mtp_weight_bytes = Wm[0].numel()
     del Wm
+    # the plain streaming read at the logit projections' weight sizes, next to their GEMV rates
+    ceil = read_ceiling(torch, qmv, dev, {"c3": c3_weight_bytes, "mtp": mtp_weight_bytes}, iters=20)
+    res["read_ceiling_logits"] = ceil
+    for row, key in (("c3_qmv_q8_0_only_262144x5376", "c3"), ("mtp_qmv_q8_0_only_262144x1024", "mtp")):
+        res[row]["frac_of_read_ceiling"] = round(res[row]["GB/s"] / ceil[key]["GB/s"], 4)
     # a plain device-to-device copy of 256 MB (read + write), next to the GEMV rates
     a = torch.empty(256 * 1000 * 1000, dtype=torch.uint8, device=dev).fill_(1)
     bb = torch.empty_like(a)
