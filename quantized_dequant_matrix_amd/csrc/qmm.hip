@@ -860,26 +860,22 @@ void qmm_f16_kernel(const uint8_t* __restrict__ W, const uint8_t* __restrict__ h
         __syncthreads();
         if (c0 + KC < kb1) fetch(c0 + KC);
         const int npair = min(KC, kb1 - c0) >> 1;
-        // Rows past M are zero in the split layout; their lanes skip the loads.
+        // Rows past M are zero in the split layout (scale 1).  Lanes of such
+        // rows all read the tile's first zero row: one address, no extra
+        // traffic, and no branch around the loads.
         auto load_a = [&](int cp, AFrag& A) {
             const int64_t b = c0 + 2 * cp;
 #pragma unroll
             for (int mi = 0; mi < MW; ++mi) {
                 const int64_t mt = tm * MW + mi;
-                const bool arow = mt * 16 + li < M;        // A operand row of this lane
-                const bool orow = mt * 16 + 4 * lg < M;    // first output row of this lane
+                const int64_t live = M - mt * 16;  // real rows of this tile (may exceed 16)
+                const int ai = (live < 16 && li > live) ? static_cast<int>(live) : li;
 #pragma unroll
                 for (int j = 0; j < 2; ++j) {
-                    h8 hv = {}, lv = {};
-                    if (arow) {
-                        const uint4* src = reinterpret_cast<const uint4*>(hl + ((mt * nb + b + j) * kWave + lane) * 32);
-                        hv = __builtin_bit_cast(h8, src[0]);
-                        lv = __builtin_bit_cast(h8, src[1]);
-                    }
-                    A.h[mi][j] = hv;
-                    A.l[mi][j] = lv;
-                    float4 sv = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-                    if (orow) sv = *reinterpret_cast<const float4*>(sx + (mt * nb + b + j) * 16 + 4 * lg);
+                    const uint4* src = reinterpret_cast<const uint4*>(hl + ((mt * nb + b + j) * kWave + ai + 16 * lg) * 32);
+                    A.h[mi][j] = __builtin_bit_cast(h8, src[0]);
+                    A.l[mi][j] = __builtin_bit_cast(h8, src[1]);
+                    const float4 sv = *reinterpret_cast<const float4*>(sx + (mt * nb + b + j) * 16 + 4 * lg);
                     A.s[mi][j][0] = sv.x; A.s[mi][j][1] = sv.y; A.s[mi][j][2] = sv.z; A.s[mi][j][3] = sv.w;
                 }
             }
