@@ -55,15 +55,12 @@ constexpr int kListRegs = 8;              // entries of its list a tournament th
 // sorted.
 constexpr int kRoundsMaxK = 16;
 
+// Branch-free (selects only), so that a run of keys can be formed after one
+// batch of loads.
 __device__ __forceinline__ uint64_t order_key(float v, uint32_t idx) {
-    uint32_t code;
-    if (v != v) {
-        code = 0u;
-    } else {
-        if (v == 0.0f) v = 0.0f;  // -0 ranks with +0
-        const uint32_t b = __float_as_uint(v);
-        code = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
-    }
+    const uint32_t b = (v == 0.0f) ? 0u : __float_as_uint(v);  // -0 ranks with +0
+    uint32_t code = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+    code = (v != v) ? 0u : code;                                // NaN after every number
     return (static_cast<uint64_t>(code) << 32) | static_cast<uint64_t>(0xFFFFFFFFu - idx);
 }
 
@@ -256,11 +253,19 @@ void topk_chunk_kernel(const float* __restrict__ y, int64_t N, int k, int nwchun
     if (c >= nwchunks) return;                                        // whole wave leaves together
     const int lane = threadIdx.x & (kWave - 1);
     const float* ym = y + static_cast<int64_t>(m) * N;
+    // all KPL loads first (indices past N read the last entry again), then
+    // the keys: one memory round trip instead of one per key
+    float v[KPL];
+#pragma unroll
+    for (int i = 0; i < KPL; ++i) {
+        const int64_t idx = (static_cast<int64_t>(c) * KPL + i) * kWave + lane;
+        v[i] = ym[idx < N ? idx : N - 1];
+    }
     uint64_t key[KPL];
 #pragma unroll
     for (int i = 0; i < KPL; ++i) {
         const int64_t idx = (static_cast<int64_t>(c) * KPL + i) * kWave + lane;
-        key[i] = idx < N ? order_key(ym[idx], static_cast<uint32_t>(idx)) : 0ull;
+        key[i] = idx < N ? order_key(v[i], static_cast<uint32_t>(idx)) : 0ull;
     }
     uint64_t* out = cand + (static_cast<int64_t>(m) * nwchunks + c) * k;
     if (KPL == 4 && k > kRoundsMaxK) {
