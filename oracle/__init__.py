@@ -297,10 +297,13 @@ def float_tol(S: np.ndarray) -> np.ndarray:
 
 # float32 evaluation of h = gelu(g) * u: |dh| <= 2^-20 |u| (|g| + |gelu(g)|).
 # The inner polynomial has no cancellation (v and 0.044715 v^3 share a sign),
-# so it carries a few float32 roundings; tanhf adds a couple of ulps and at
-# most 0.45 times the inner's relative error; 1 + t, the two products and the
-# factor 1/2 add a few more: about 8 units of 2^-24 on |g| |u| and 2 on |h|.
-# 2^-20 = 16 units leaves a factor-2 margin over that count.
+# so it carries a few float32 roundings.  Evaluated as v/2 (1 + tanhf(z)),
+# tanhf adds a couple of ulps and at most 0.45 times the inner's relative
+# error, and 1 + t, the products and the halving a few more: about 8 units of
+# 2^-24 on |g| |u|.  Evaluated as the same function v / (1 + e^(-2z)), the
+# exponential, sum, reciprocal and products add about 6 units on |gelu(g)| |u|,
+# and the rounding of the exponent's argument at most 0.37 units on |g| |u|
+# (x e^-x <= 1/e).  2^-20 = 16 units leaves a factor-2 margin over either.
 H_F32_REL = 2.0**-20
 
 

@@ -77,12 +77,19 @@ __device__ __forceinline__ float wave_sum(float v) {
     return v;
 }
 
-// GELU, tanh form: v/2 (1 + tanh(sqrt(2/pi) (v + 0.044715 v^3))).
-// tanhf(+-inf) = +-1, so an overflowing cube gives v or -0, never NaN.
+// GELU, tanh form: v/2 (1 + tanh z), z = sqrt(2/pi) (v + 0.044715 v^3).
+// Evaluated as v / (1 + e^(-2z)), the same function (1 + tanh z =
+// 2 / (1 + e^(-2z))) without the cancellation of 1 + tanh z near z << 0,
+// with e^(-2z) = 2^(-2z log2 e) from v_exp_f32 and the quotient from
+// v_rcp_f32: a few instructions instead of a tanhf call.  Error: a few ulp
+// of the result, plus the exponent argument's rounding, which matters only
+// where the result is below e^-1 |v| 2^-24.  e^(-2z) overflowing to +inf
+// gives -0 for v << 0, and underflowing to 0 gives v: never NaN.
 __device__ __forceinline__ float gelu_tanh(float v) {
     const float c = 0.7978845608028654f;  // sqrt(2/pi)
     const float inner = c * (v + 0.044715f * v * v * v);
-    return 0.5f * v * (1.0f + tanhf(inner));
+    const float e = __builtin_amdgcn_exp2f(-2.8853900817779268f * inner);  // -2 log2(e) z
+    return v * __builtin_amdgcn_rcpf(1.0f + e);
 }
 
 }  // namespace qmv
