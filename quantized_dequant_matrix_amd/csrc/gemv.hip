@@ -779,10 +779,11 @@ hipError_t launch_unit(const void* W0, const void* W1, const float* x, const flo
     // One matrix at a time runs best with 3 workgroups per CU, all resident
     // at once, its waves taking several passes each: a wave's first loads
     // then share the memory system with fewer others and arrive sooner.  The
-    // pair (4 resident per CU at its 123 VGPRs) runs best with one pass per
+    // pair (4 resident per CU at its 123 VGPRs) and Q6_K, whose passes carry
+    // the most bytes (18 and 13.4 KB per wave), run best with one pass per
     // wave and workgroups replacing each other as they finish (1792 at the
     // gate shape), up to 8 per CU before waves loop.
-    const int max_blocks = device_cus() * (PAIR ? 8 : 3);
+    const int max_blocks = device_cus() * ((PAIR || F == kQ6_K) ? 8 : 3);
     int blocks = (npasses + kWavesPerBlock - 1) / kWavesPerBlock;
     if (blocks > max_blocks) blocks = max_blocks;
     const size_t lds = static_cast<size_t>(G) * kXsStride * sizeof(float);
