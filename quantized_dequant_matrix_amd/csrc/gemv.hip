@@ -413,7 +413,6 @@ __global__ __launch_bounds__(kBlockThreads) __attribute__((amdgpu_waves_per_eu(k
 void gemv_unit_kernel(const uint8_t* __restrict__ W0, const uint8_t* __restrict__ W1,
                       const float* __restrict__ x, const float* __restrict__ xu, float* __restrict__ y,
                       int N, int G, int S, int npasses) {
-    constexpr int VEC = UnitInfo<F>::kVec;
     constexpr int UB = UnitInfo<F>::kBytes;
     constexpr int NM = PAIR ? 2 : 1;
     extern __shared__ float xs[];
