@@ -188,6 +188,30 @@ def test_zero_weights_exactly_zero():
     assert np.all(y == 0.0)
 
 
+@pytest.mark.parametrize("fmt", FMTS)
+def test_non_finite_activations(fmt):
+    """IEEE semantics as in the float64 oracle: an infinite activation gives
+    +-inf in the rows whose weight there is nonzero and NaN (inf * 0) where it
+    is zero; a NaN activation makes every row NaN.  The finite entries keep
+    the usual bound."""
+    N, K = 96, 768
+    say(f"qmv_{fmt} non-finite activations")
+    W, x = synth.problem(fmt, N, K, 1, 31)
+    for pos, val in ((5, np.inf), (300, -np.inf), (17, np.nan)):
+        xs = x.copy()
+        xs[0, pos] = val
+        y = run_gemv(fmt, W, xs, N, K)[0]
+        with np.errstate(invalid="ignore", over="ignore"):
+            yr, S = oracle.qmv(fmt, W, N, K, xs)
+        yr = yr[0]
+        assert np.array_equal(np.isnan(y), np.isnan(yr)), (fmt, pos)
+        assert np.array_equal(np.isposinf(y), np.isposinf(yr)), (fmt, pos)
+        assert np.array_equal(np.isneginf(y), np.isneginf(yr)), (fmt, pos)
+        fin = np.isfinite(yr)
+        if fin.any():
+            assert_within(y[None, fin], yr[None, fin], oracle.float_tol(S[0][fin])[None, :], f"{fmt} finite rows")
+
+
 def test_wide_dynamic_range():
     N, K = 40, 4096
     say("qmv wide dynamic range activations")
