@@ -104,3 +104,22 @@ def test_batched_rows():
     y = run(codes, scales, x, N, K, M)
     yr, S = oracle.qmv_mxfp4(codes, scales, N, K, x, M=M)
     assert_within(y, yr, oracle.float_tol(S), "M=3")
+
+
+@pytest.mark.parametrize("K", [768, 21504])
+def test_non_finite_activations(K):
+    # as the float64 oracle: inf gives +-inf, or NaN where the weight is 0
+    # (or the block scale is NaN); a NaN activation makes every row NaN
+    N = 64
+    say(f"qmv_mxfp4 non-finite activations K={K}")
+    codes, scales, x = synth.mxfp4_problem(N, K, 1, 57)
+    for pos, val in ((9, np.inf), (400, -np.inf), (33, np.nan)):
+        xs = x.copy()
+        xs[0, pos] = val
+        y = run(codes, scales, xs, N, K)[0]
+        with np.errstate(invalid="ignore", over="ignore"):
+            yr, S = oracle.qmv_mxfp4(codes, scales, N, K, xs)
+        yr = yr[0]
+        assert np.array_equal(np.isnan(y), np.isnan(yr)), pos
+        assert np.array_equal(np.isposinf(y), np.isposinf(yr)), pos
+        assert np.array_equal(np.isneginf(y), np.isneginf(yr)), pos
