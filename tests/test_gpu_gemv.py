@@ -276,6 +276,25 @@ def test_geglu_batched_and_large_gate():
     assert_within(h, hr, tol, "geglu batched")
 
 
+def test_geglu_non_finite():
+    # gelu(+inf) = +inf and gelu(-inf) = -inf * 0 = NaN in the float64 tanh
+    # form; with u = +-inf or NaN the product classes follow.  Same on the GPU.
+    N, K = 64, 5376
+    say("qmv_q4_0_geglu non-finite activations")
+    Wg, x = synth.problem("q4_0", N, K, 1, 71)
+    Wu = synth.q4_0_weights(N, K, 72)
+    for pos, val in ((11, np.inf), (2000, -np.inf), (37, np.nan)):
+        xs = x.copy()
+        xs[0, pos] = val
+        h = run_geglu(Wg, Wu, xs, N, K)[0]
+        with np.errstate(invalid="ignore", over="ignore"):
+            hr, _ = geglu_ref(Wg, Wu, xs, N, K)
+        hr = hr.reshape(-1)
+        assert np.array_equal(np.isnan(h), np.isnan(hr)), pos
+        assert np.array_equal(np.isposinf(h), np.isposinf(hr)), pos
+        assert np.array_equal(np.isneginf(h), np.isneginf(hr)), pos
+
+
 def test_geglu_workload_full():
     c = synth.CONFIGS["c2"]
     say("qmv_q4_0_geglu workload pair 21504x5376")
