@@ -108,3 +108,23 @@ def test_same_as_plain_product_of_staged_h():
     yp = empty((1, N))
     _qmv().qmv_q6_k(dev(W), dev(np.full((1, K), 64.0, np.float32)), yp, N, K, 1)
     assert np.array_equal(y, host(yp))
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("K", [5376, 21504])
+def test_non_finite_inputs(fmt, K):
+    # h = gelu(g) * u staged in float32: gelu(+inf) = inf, gelu(-inf) = NaN,
+    # and the output classes follow the float64 oracle row by row
+    N = 48
+    say(f"qmv_{fmt}_geglu_down non-finite inputs K={K}")
+    W, g, u = problem(fmt, N, K, 1, 91)
+    for which, pos, val in (("g", 7, np.inf), ("g", 300, -np.inf), ("u", 40, np.inf), ("u", 41, np.nan)):
+        gs, us = g.copy(), u.copy()
+        (gs if which == "g" else us)[0, pos] = val
+        y = run_down(fmt, W, gs, us, N, K)[0]
+        with np.errstate(invalid="ignore", over="ignore"):
+            yr, _, _ = oracle.qmv_geglu_down(fmt, W, N, K, gs, us)
+        yr = yr[0]
+        assert np.array_equal(np.isnan(y), np.isnan(yr)), (which, pos)
+        assert np.array_equal(np.isposinf(y), np.isposinf(yr)), (which, pos)
+        assert np.array_equal(np.isneginf(y), np.isneginf(yr)), (which, pos)
