@@ -248,10 +248,20 @@ int logits_sample(const void* W_q8_0, const float* x, const float* u, int32_t* t
 int qmvdbg_quantize_q8(const float* x, int8_t* q, float* d,
                        int64_t K, int64_t M, hipStream_t stream);
 
-/* Integer block sums of qmm_q4_0_q8act for given int8 activations, from the
- * same kernels (same M-dependent choice): isum int32 [M][N][K/32]. */
-int qmvdbg_q4_0_q8_blocksums(const void* W, const int8_t* qx, int32_t* isum,
-                             int64_t N, int64_t K, int64_t M, hipStream_t stream);
+/* The integer block sums of qmm_q4_0_q8act, from the launches that
+ * qmm_q4_0_q8act(W, x, y, N, K, M, ws, ws_bytes) makes: the same
+ * quantization of x into ws, the same kernel (v_dot4 for M == 1, the narrow
+ * or the wide int8 MFMA tiling for M >= 2, chosen by (N, K, M) alone) on the
+ * same grid, with the float epilogue y += isum * d_w * d_x replaced by a
+ * store of the exact block sums of the rows n0 <= n < n1:
+ *   isum[m][n - n0][b] = sum_{j < 32} (q_w[n][32 b + j] - 8) * q_x[m][32 b + j]
+ * (int32 [M][n1 - n0][K/32]).  y is not written.  0 <= n0 < n1 <= N, else
+ * QMV_ERR_ARG; other arguments and errors as qmm_q4_0_q8act.
+ * [captable section 1: q4_matvec_v4, Q4_0 x Q8 int8 block dot products;
+ *  roadmap K3: batched Q4_0 matrix-matrix prefill] */
+int qmvdbg_qmm_q4_0_q8act_blocksums(const void* W, const float* x, int32_t* isum,
+                                    int64_t N, int64_t K, int64_t M, int64_t n0, int64_t n1,
+                                    void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* The top-k stages of logits_topk on a given float32 vector y [M][N]:
  * same ordering rule, values returned as softcap * tanh(y / softcap). */

@@ -118,7 +118,7 @@ template <bool WRITE_ISUM>
 __global__ __launch_bounds__(kBlockThreads)
 void qmm_dot_kernel(const uint8_t* __restrict__ W, const int8_t* __restrict__ qx,
                     const float* __restrict__ dx, float* __restrict__ y, int32_t* __restrict__ isum,
-                    int N, int G, int C, int L, int S, int npasses, int m0) {
+                    int N, int G, int C, int L, int S, int npasses, int m0, int isn0, int isn1) {
     extern __shared__ __align__(16) unsigned char lds[];
     const int m = m0 + blockIdx.y;
     const int64_t K = static_cast<int64_t>(G) * kUnitElems;
@@ -132,7 +132,7 @@ void qmm_dot_kernel(const uint8_t* __restrict__ W, const int8_t* __restrict__ qx
         const uint4 v = reinterpret_cast<const uint4*>(qxm)[i];
         *reinterpret_cast<uint4*>(qs + (i >> 4) * kQxStride + (i & 15) * 16) = v;
     }
-    // the block-sum export passes no scales (dx == nullptr) and never reads ds
+    // the block-sum mode reads no scales
     if constexpr (!WRITE_ISUM) {
         for (int i = threadIdx.x; i < nb; i += kBlockThreads) ds[i] = dx[static_cast<int64_t>(m) * nb + i];
     }
@@ -188,7 +188,8 @@ void qmm_dot_kernel(const uint8_t* __restrict__ W, const int8_t* __restrict__ qx
                 }
                 const int blk = u * 8 + k;
                 if constexpr (WRITE_ISUM) {
-                    if (ok) isum[(static_cast<int64_t>(m) * N + row) * nb + blk] = s16 >> 4;
+                    if (ok && row >= isn0 && row < isn1)
+                        isum[(static_cast<int64_t>(m) * (isn1 - isn0) + (row - isn0)) * nb + blk] = s16 >> 4;
                 } else {
                     const float scale = half_bits_to_float(dbits) * 0.0625f * ds[blk];
                     acc = fmaf(static_cast<float>(s16), scale, acc);
@@ -208,7 +209,7 @@ template <bool WRITE_ISUM>
 __global__ __launch_bounds__(kBlockThreads)
 void qmm_generic_kernel(const uint8_t* __restrict__ W, const int8_t* __restrict__ qx,
                         const float* __restrict__ dx, float* __restrict__ y, int32_t* __restrict__ isum,
-                        int64_t N, int64_t K, int64_t M) {
+                        int64_t N, int64_t K, int64_t M, int64_t isn0, int64_t isn1) {
     const int lane = threadIdx.x & (kWave - 1);
     const int64_t nb = K / 32;
     const int64_t row_bytes = nb * 18;
@@ -233,7 +234,7 @@ void qmm_generic_kernel(const uint8_t* __restrict__ W, const int8_t* __restrict_
                 s16 = __builtin_amdgcn_sdot4(static_cast<int>(hi), static_cast<int>(xq[4 + t]), s16, false);
             }
             if constexpr (WRITE_ISUM) {
-                isum[(m * N + row) * nb + b] = s16 >> 4;
+                if (row >= isn0 && row < isn1) isum[(m * (isn1 - isn0) + (row - isn0)) * nb + b] = s16 >> 4;
             } else {
                 acc = fmaf(static_cast<float>(s16), half_bits_to_float(blk[0]) * 0.0625f * dx[m * nb + b], acc);
             }
@@ -298,7 +299,7 @@ __global__ __launch_bounds__(kBlockThreads)
 void qmm_mfma_kernel(const uint8_t* __restrict__ W, const int8_t* __restrict__ xa,
                      const float* __restrict__ xd, float* __restrict__ out, int32_t* __restrict__ isum,
                      int N, int64_t M, int nb, int64_t tm0, int64_t tiles_m, int tiles_n, int kb_per,
-                     int64_t nwg) {
+                     int64_t nwg, int isn0, int isn1) {
     constexpr int TN = 16 * NW * WN;
     constexpr int RB = KC * 18;       // bytes of one weight row per chunk
     constexpr int RS = RB + 16;       // LDS row stride: rows 4 banks apart (mod 64)
@@ -320,7 +321,6 @@ void qmm_mfma_kernel(const uint8_t* __restrict__ W, const int8_t* __restrict__ x
     const int kb0 = ks * kb_per;
     const int kb1 = min(nb, kb0 + kb_per);
     const int n0 = tn * TN;
-    const int64_t K = static_cast<int64_t>(nb) * 32;
     const int64_t row_bytes = static_cast<int64_t>(nb) * 18;
 
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
@@ -384,17 +384,10 @@ void qmm_mfma_kernel(const uint8_t* __restrict__ W, const int8_t* __restrict__ x
 #pragma unroll
             for (int mi = 0; mi < MW; ++mi) {
                 const int64_t mt = tm * (MW * WM) + wm * MW + mi;  // 16-row tile
-                if constexpr (MODE == kModeISum) {
-                    // row-major codes [M][K] (rows past M: any valid row)
-                    int64_t m = mt * 16 + li;
-                    m = m < M ? m : M - 1;
-                    const uint32_t* src = reinterpret_cast<const uint32_t*>(xa + m * K + 32 * b);
-                    A.e[mi] = static_cast<uint64_t>(src[lg]) | (static_cast<uint64_t>(src[4 + lg]) << 32);
-                    A.o[mi] = static_cast<uint64_t>(src[8 + lg]) | (static_cast<uint64_t>(src[12 + lg]) << 32);
-                } else {
-                    const uint4 v = *reinterpret_cast<const uint4*>(xa + ((mt * (nb >> 1) + (b >> 1)) * kWave + lane) * 16);
-                    A.e[mi] = static_cast<uint64_t>(v.x) | (static_cast<uint64_t>(v.y) << 32);
-                    A.o[mi] = static_cast<uint64_t>(v.z) | (static_cast<uint64_t>(v.w) << 32);
+                const uint4 v = *reinterpret_cast<const uint4*>(xa + ((mt * (nb >> 1) + (b >> 1)) * kWave + lane) * 16);
+                A.e[mi] = static_cast<uint64_t>(v.x) | (static_cast<uint64_t>(v.y) << 32);
+                A.o[mi] = static_cast<uint64_t>(v.z) | (static_cast<uint64_t>(v.w) << 32);
+                if constexpr (MODE != kModeISum) {
                     const float4 de = *reinterpret_cast<const float4*>(xd + (mt * nb + b) * 16 + 4 * lg);
                     const float4 dq = *reinterpret_cast<const float4*>(xd + (mt * nb + b + 1) * 16 + 4 * lg);
                     A.xe[mi][0] = de.x; A.xe[mi][1] = de.y; A.xe[mi][2] = de.z; A.xe[mi][3] = de.w;
@@ -434,8 +427,8 @@ void qmm_mfma_kernel(const uint8_t* __restrict__ W, const int8_t* __restrict__ x
 #pragma unroll
                         for (int r = 0; r < 4; ++r) {
                             const int64_t m = (tm * (MW * WM) + wm * MW + mi) * 16 + 4 * lg + r;
-                            if (m < M && n < N) {
-                                int32_t* dst = isum + (m * N + n) * nb + b;
+                            if (m < M && n >= isn0 && n < isn1) {
+                                int32_t* dst = isum + (m * (isn1 - isn0) + (n - isn0)) * nb + b;
                                 dst[0] = De[r] >> 4;
                                 dst[1] = Do[r] >> 4;
                             }
@@ -523,11 +516,17 @@ void qmm_mfma_kernel(const uint8_t* __restrict__ W, const int8_t* __restrict__ x
 //     whole [M, K] set stays in the caches), one block pair ahead of the
 //     multiplies, with unconditional loads so that no branch merges the
 //     waits (the pair after the last one re-reads the last pair).
-template <int KC>
+//
+// MODE kModeISum replaces the float epilogue by a store of the exact block
+// sums of the rows n in [isn0, isn1) (isum [M][isn1 - isn0][nb]); every other
+// step -- the grid, the weight stash and decode, the operand layouts and the
+// MFMAs -- is the one that computes y.
+template <int KC, int MODE>
 __global__ __launch_bounds__(kBlockThreads)
 void qmm_wide_kernel(const uint8_t* __restrict__ W, const int8_t* __restrict__ xa, const float* __restrict__ xd,
-                     float* __restrict__ out, int N, int64_t M, int nb, int64_t tm0, int64_t tiles_m, int tiles_n,
-                     int64_t nwg) {
+                     float* __restrict__ out, int32_t* __restrict__ isum, int N, int64_t M, int nb, int64_t tm0,
+                     int64_t tiles_m, int tiles_n, int64_t nwg, int isn0, int isn1) {
+    static_assert(MODE == kModeY || MODE == kModeISum, "y or block sums");
     constexpr int MW = 2, NW = 2, WM = 2, WN = 2;
     constexpr int TN = 16 * NW * WN;           // 64 weight rows
     constexpr int kGroupStride = 2 * TN + 32;  // dwords: k-groups 32 banks apart
@@ -627,8 +626,8 @@ void qmm_wide_kernel(const uint8_t* __restrict__ W, const int8_t* __restrict__ x
 #pragma unroll
             for (int r = 0; r < 4; ++r) acc[mi][ni][r] = 0.0f;
 
-    // block pair jp of the chunk in LDS, activations from A
-    auto mul_pair = [&](int jp, const AFrag& A) {
+    // block pair jp of the chunk in LDS (blocks b, b + 1 of the row), activations from A
+    auto mul_pair = [&](int jp, const AFrag& A, int64_t b) {
         const int je = 2 * jp, jo = 2 * jp + 1;
 #pragma unroll
         for (int ni = 0; ni < NW; ++ni) {
@@ -646,10 +645,23 @@ void qmm_wide_kernel(const uint8_t* __restrict__ W, const int8_t* __restrict__ x
                                                                       zero, 0, 0, 0);
                 const v4i Do = __builtin_amdgcn_mfma_i32_16x16x32_i8(static_cast<long>(A.o[mi]), static_cast<long>(bo),
                                                                       zero, 0, 0, 0);
+                if constexpr (MODE == kModeISum) {
+                    const int n = n0 + r;
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    acc[mi][ni][q] = fmaf(static_cast<float>(De[q]), se * A.xe[mi][q], acc[mi][ni][q]);
-                    acc[mi][ni][q] = fmaf(static_cast<float>(Do[q]), so * A.xo[mi][q], acc[mi][ni][q]);
+                    for (int q = 0; q < 4; ++q) {
+                        const int64_t m = (tm * (MW * WM) + wm * MW + mi) * 16 + 4 * lg + q;
+                        if (m < M && n >= isn0 && n < isn1) {
+                            int32_t* dst = isum + (m * (isn1 - isn0) + (n - isn0)) * nb + b;
+                            dst[0] = De[q] >> 4;
+                            dst[1] = Do[q] >> 4;
+                        }
+                    }
+                } else {
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        acc[mi][ni][q] = fmaf(static_cast<float>(De[q]), se * A.xe[mi][q], acc[mi][ni][q]);
+                        acc[mi][ni][q] = fmaf(static_cast<float>(Do[q]), so * A.xo[mi][q], acc[mi][ni][q]);
+                    }
                 }
             }
         }
@@ -666,23 +678,25 @@ void qmm_wide_kernel(const uint8_t* __restrict__ W, const int8_t* __restrict__ x
         const int npair = min(KC, nb - c0) >> 1;  // 4 or 8: even
         for (int jp = 0; jp < npair; jp += 2) {
             load_a(c0 + 2 * jp + 2, A1);
-            mul_pair(jp, A0);
+            mul_pair(jp, A0, c0 + 2 * jp);
             const int64_t nxt = c0 + 2 * jp + 4;
             load_a(nxt < nb ? nxt : nb - 2, A0);
-            mul_pair(jp + 1, A1);
+            mul_pair(jp + 1, A1, c0 + 2 * jp + 2);
         }
     }
+    if constexpr (MODE == kModeY) {
 #pragma unroll
-    for (int mi = 0; mi < MW; ++mi)
+        for (int mi = 0; mi < MW; ++mi)
 #pragma unroll
-        for (int ni = 0; ni < NW; ++ni) {
-            const int n = n0 + (wn * NW + ni) * 16 + li;
+            for (int ni = 0; ni < NW; ++ni) {
+                const int n = n0 + (wn * NW + ni) * 16 + li;
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int64_t m = (tm * (MW * WM) + wm * MW + mi) * 16 + 4 * lg + q;
-                if (m < M && n < N) out[m * N + n] = acc[mi][ni][q];
+                for (int q = 0; q < 4; ++q) {
+                    const int64_t m = (tm * (MW * WM) + wm * MW + mi) * 16 + 4 * lg + q;
+                    if (m < M && n < N) out[m * N + n] = acc[mi][ni][q];
+                }
             }
-        }
+    }
 }
 
 // ------------------------------------------------ float32 activations
@@ -1042,7 +1056,8 @@ hipError_t launch_quantize(const float* x, int8_t* q, float* d, int64_t K, int64
 
 template <int MW, int NW, int WM, int WN, int WK, int KC, int MODE>
 hipError_t launch_mfma(const QmmPlan& p, const void* W, const int8_t* xa, const float* xd, float* out,
-                       int32_t* isum, int64_t N, int64_t K, int64_t M, hipStream_t stream) {
+                       int32_t* isum, int64_t isn0, int64_t isn1, int64_t N, int64_t K, int64_t M,
+                       hipStream_t stream) {
     // slices of m-tiles keep the grid within 2^30 workgroups
     const int64_t per_mt = static_cast<int64_t>(p.tiles_n) * p.ks;
     int64_t mt_slice = (int64_t{1} << 30) / per_mt;
@@ -1052,7 +1067,8 @@ hipError_t launch_mfma(const QmmPlan& p, const void* W, const int8_t* xa, const 
         const int64_t nwg = tms * per_mt;
         hipLaunchKernelGGL((qmm_mfma_kernel<MW, NW, WM, WN, WK, KC, MODE>), dim3(static_cast<unsigned>(nwg)),
                            dim3(kBlockThreads), 0, stream, static_cast<const uint8_t*>(W), xa, xd, out, isum,
-                           static_cast<int>(N), M, static_cast<int>(K / 32), tm0, tms, p.tiles_n, p.kb, nwg);
+                           static_cast<int>(N), M, static_cast<int>(K / 32), tm0, tms, p.tiles_n, p.kb, nwg,
+                           static_cast<int>(isn0), static_cast<int>(isn1));
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
@@ -1061,16 +1077,19 @@ hipError_t launch_mfma(const QmmPlan& p, const void* W, const int8_t* xa, const 
 
 // The wide path: qmm_wide_kernel over all tiles, in slices of m-tiles that
 // keep the grid within 2^30 workgroups.
-hipError_t launch_wide(const QmmPlan& p, const void* W, const int8_t* xa, const float* xd, float* y, int64_t N,
-                       int64_t K, int64_t M, hipStream_t stream) {
+template <int MODE>
+hipError_t launch_wide(const QmmPlan& p, const void* W, const int8_t* xa, const float* xd, float* y,
+                       int32_t* isum, int64_t isn0, int64_t isn1, int64_t N, int64_t K, int64_t M,
+                       hipStream_t stream) {
     int64_t mt_slice = (int64_t{1} << 30) / p.tiles_n;
     mt_slice = mt_slice < p.tiles_m ? mt_slice : p.tiles_m;
     for (int64_t tm0 = 0; tm0 < p.tiles_m; tm0 += mt_slice) {
         const int64_t tms = (p.tiles_m - tm0 < mt_slice) ? p.tiles_m - tm0 : mt_slice;
         const int64_t nwg = tms * p.tiles_n;
-        hipLaunchKernelGGL((qmm_wide_kernel<16>), dim3(static_cast<unsigned>(nwg)), dim3(kBlockThreads), 0, stream,
-                           static_cast<const uint8_t*>(W), xa, xd, y, static_cast<int>(N), M, static_cast<int>(K / 32),
-                           tm0, tms, p.tiles_n, nwg);
+        hipLaunchKernelGGL((qmm_wide_kernel<16, MODE>), dim3(static_cast<unsigned>(nwg)), dim3(kBlockThreads), 0,
+                           stream, static_cast<const uint8_t*>(W), xa, xd, y, isum, static_cast<int>(N), M,
+                           static_cast<int>(K / 32), tm0, tms, p.tiles_n, nwg, static_cast<int>(isn0),
+                           static_cast<int>(isn1));
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
@@ -1138,17 +1157,17 @@ hipError_t launch_f16(const F32ActPlan& p, const void* W, const uint8_t* hl, con
 
 // The M == 1 and K % 256 != 0 paths (row-major activation codes).
 hipError_t launch_dot(const QmmPlan& p, const void* W, const int8_t* qx, const float* dx, float* y, int32_t* isum,
-                      int64_t N64, int64_t K, int64_t M, hipStream_t stream) {
+                      int64_t isn0, int64_t isn1, int64_t N64, int64_t K, int64_t M, hipStream_t stream) {
     if (p.path == kPathGeneric) {
         int64_t blocks = (N64 * M + kWavesPerBlock - 1) / kWavesPerBlock;
         const int64_t cap = static_cast<int64_t>(device_cus()) * 8;
         if (blocks > cap) blocks = cap;
         if (isum) {
             hipLaunchKernelGGL((qmm_generic_kernel<true>), dim3(static_cast<unsigned>(blocks)), dim3(kBlockThreads),
-                               0, stream, static_cast<const uint8_t*>(W), qx, dx, y, isum, N64, K, M);
+                               0, stream, static_cast<const uint8_t*>(W), qx, dx, y, isum, N64, K, M, isn0, isn1);
         } else {
             hipLaunchKernelGGL((qmm_generic_kernel<false>), dim3(static_cast<unsigned>(blocks)), dim3(kBlockThreads),
-                               0, stream, static_cast<const uint8_t*>(W), qx, dx, y, isum, N64, K, M);
+                               0, stream, static_cast<const uint8_t*>(W), qx, dx, y, isum, N64, K, M, isn0, isn1);
         }
         return hipGetLastError();
     }
@@ -1166,11 +1185,11 @@ hipError_t launch_dot(const QmmPlan& p, const void* W, const int8_t* qx, const f
         if (isum) {
             hipLaunchKernelGGL((qmm_dot_kernel<true>), dim3(blocks, static_cast<unsigned>(mc)), dim3(kBlockThreads),
                                lds, stream, static_cast<const uint8_t*>(W), qx, dx, y, isum, N, G, C, L, S,
-                               npasses, static_cast<int>(m0));
+                               npasses, static_cast<int>(m0), static_cast<int>(isn0), static_cast<int>(isn1));
         } else {
             hipLaunchKernelGGL((qmm_dot_kernel<false>), dim3(blocks, static_cast<unsigned>(mc)), dim3(kBlockThreads),
                                lds, stream, static_cast<const uint8_t*>(W), qx, dx, y, isum, N, G, C, L, S,
-                               npasses, static_cast<int>(m0));
+                               npasses, static_cast<int>(m0), static_cast<int>(isn0), static_cast<int>(isn1));
         }
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
@@ -1189,8 +1208,8 @@ hipError_t launch_quantize_q8(const float* x, int8_t* q, float* d, int64_t K, in
     return launch_quantize<false>(x, q, d, K, M, M, stream);
 }
 
-hipError_t launch_qmm_q8act(const void* W, const float* x, float* y, int64_t N, int64_t K, int64_t M, void* ws,
-                            hipStream_t stream) {
+hipError_t launch_qmm_q8act(const void* W, const float* x, float* y, int32_t* isum, int64_t isn0, int64_t isn1,
+                            int64_t N, int64_t K, int64_t M, void* ws, hipStream_t stream) {
     const QmmPlan p = plan_qmm(N, K, M);
     int8_t* q = static_cast<int8_t*>(ws);
     float* d = reinterpret_cast<float*>(static_cast<char*>(ws) + p.q_bytes);
@@ -1199,10 +1218,15 @@ hipError_t launch_qmm_q8act(const void* W, const float* x, float* y, int64_t N, 
     hipError_t e = mfma ? launch_quantize<true>(x, q, d, K, M, p.xrows, stream)
                         : launch_quantize<false>(x, q, d, K, M, M, stream);
     if (e != hipSuccess) return e;
-    if (!mfma) return launch_dot(p, W, q, d, y, nullptr, N, K, M, stream);
-    if (p.path == kPathWide) return launch_wide(p, W, q, d, y, N, K, M, stream);
-    if (p.ks == 1) return launch_mfma<QMM_NARROW, kModeY>(p, W, q, d, y, nullptr, N, K, M, stream);
-    e = launch_mfma<QMM_NARROW, kModePartial>(p, W, q, d, part, nullptr, N, K, M, stream);
+    if (!mfma) return launch_dot(p, W, q, d, isum ? nullptr : y, isum, isn0, isn1, N, K, M, stream);
+    if (p.path == kPathWide) {
+        return isum ? launch_wide<kModeISum>(p, W, q, d, nullptr, isum, isn0, isn1, N, K, M, stream)
+                    : launch_wide<kModeY>(p, W, q, d, y, nullptr, 0, 0, N, K, M, stream);
+    }
+    // the narrow tiling: the block-sum mode runs the same grid, K splits included
+    if (isum) return launch_mfma<QMM_NARROW, kModeISum>(p, W, q, d, nullptr, isum, isn0, isn1, N, K, M, stream);
+    if (p.ks == 1) return launch_mfma<QMM_NARROW, kModeY>(p, W, q, d, y, nullptr, 0, 0, N, K, M, stream);
+    e = launch_mfma<QMM_NARROW, kModePartial>(p, W, q, d, part, nullptr, 0, 0, N, K, M, stream);
     if (e != hipSuccess) return e;
     const int64_t MN = M * N;
     int64_t blocks = ceil_div(MN, kBlockThreads);
@@ -1211,15 +1235,6 @@ hipError_t launch_qmm_q8act(const void* W, const float* x, float* y, int64_t N, 
     hipLaunchKernelGGL(qmm_reduce_kernel, dim3(static_cast<unsigned>(blocks)), dim3(kBlockThreads), 0, stream,
                        part, y, p.ks, MN);
     return hipGetLastError();
-}
-
-hipError_t launch_q4_0_q8_blocksums(const void* W, const int8_t* qx, int32_t* isum, int64_t N, int64_t K, int64_t M,
-                                    hipStream_t stream) {
-    const QmmPlan p = plan_qmm(N, K, M);
-    if (p.path == kPathWide) return launch_mfma<QMM_WIDE, kModeISum>(p, W, qx, nullptr, nullptr, isum, N, K, M, stream);
-    if (p.path == kPathNarrow)
-        return launch_mfma<QMM_NARROW, kModeISum>(p, W, qx, nullptr, nullptr, isum, N, K, M, stream);
-    return launch_dot(p, W, qx, nullptr, nullptr, isum, N, K, M, stream);
 }
 
 size_t qmm_f32act_ws_bytes(int64_t N, int64_t K, int64_t M) {

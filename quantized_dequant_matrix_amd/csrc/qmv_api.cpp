@@ -163,7 +163,7 @@ int qmm_q4_0_q8act(const void* W, const float* x, float* y, int64_t N, int64_t K
     if (rc) return rc;
     if (!aligned(W, 16) || !aligned(x, 4) || !aligned(y, 4) || !aligned(ws, 16)) return QMV_ERR_ALIGN;
     if (ws_bytes < qmm_q4_0_q8act_ws_bytes(N, K, M)) return QMV_ERR_WORKSPACE;
-    return launched(qmv::launch_qmm_q8act(W, x, y, N, K, M, ws, stream));
+    return launched(qmv::launch_qmm_q8act(W, x, y, nullptr, 0, 0, N, K, M, ws, stream));
 }
 
 size_t qmm_q4_0_f32act_ws_bytes(int64_t N, int64_t K, int64_t M) {
@@ -256,15 +256,17 @@ int qmvdbg_quantize_q8(const float* x, int8_t* q, float* d, int64_t K, int64_t M
     return launched(qmv::launch_quantize_q8(x, q, d, K, M, stream));
 }
 
-int qmvdbg_q4_0_q8_blocksums(const void* W, const int8_t* qx, int32_t* isum, int64_t N, int64_t K, int64_t M,
-                             hipStream_t stream) {
-    if (!W || !qx || !isum) return QMV_ERR_NULL;
+int qmvdbg_qmm_q4_0_q8act_blocksums(const void* W, const float* x, int32_t* isum, int64_t N, int64_t K, int64_t M,
+                                    int64_t n0, int64_t n1, void* ws, size_t ws_bytes, hipStream_t stream) {
+    if (!W || !x || !isum || !ws) return QMV_ERR_NULL;
     int rc = check_shape(N, K, M, 32, 18);
     if (rc) return rc;
+    if (n0 < 0 || n1 <= n0 || n1 > N) return QMV_ERR_ARG;
     int64_t t;
-    if (!mul_ok(M, N, &t) || !mul_ok(t, (K / 32) * 4, &t)) return QMV_ERR_SHAPE;
-    if (!aligned(W, 16) || !aligned(qx, 16) || !aligned(isum, 4)) return QMV_ERR_ALIGN;
-    return launched(qmv::launch_q4_0_q8_blocksums(W, qx, isum, N, K, M, stream));
+    if (!mul_ok(M, n1 - n0, &t) || !mul_ok(t, (K / 32) * 4, &t)) return QMV_ERR_SHAPE;
+    if (!aligned(W, 16) || !aligned(x, 4) || !aligned(isum, 4) || !aligned(ws, 16)) return QMV_ERR_ALIGN;
+    if (ws_bytes < qmm_q4_0_q8act_ws_bytes(N, K, M)) return QMV_ERR_WORKSPACE;
+    return launched(qmv::launch_qmm_q8act(W, x, nullptr, isum, n0, n1, N, K, M, ws, stream));
 }
 
 int qmvdbg_topk_f32(const float* y, float* top_val, int32_t* top_idx, int64_t N, int64_t M, int32_t k,

@@ -47,13 +47,12 @@ size_t qmm_ws_bytes(int64_t N, int64_t K, int64_t M);
 // Row-major codes [M][K] and scales [M][K/32] (step 1 alone).
 hipError_t launch_quantize_q8(const float* x, int8_t* q, float* d, int64_t K, int64_t M,
                               hipStream_t stream);
-// Both steps: quantize x into ws, then y = the scaled block sums.
-hipError_t launch_qmm_q8act(const void* W, const float* x, float* y, int64_t N, int64_t K, int64_t M,
-                            void* ws, hipStream_t stream);
-// int32 block sums [M][N][K/32] of row-major int8 activations, from the
-// kernel the same (N, K, M) selects in launch_qmm_q8act.
-hipError_t launch_q4_0_q8_blocksums(const void* W, const int8_t* qx, int32_t* isum, int64_t N,
-                                    int64_t K, int64_t M, hipStream_t stream);
+// Both steps: quantize x into ws, then y = the scaled block sums.  With
+// isum != nullptr the same plan, kernels and grids run with the float
+// epilogue replaced by a store of the int32 block sums of rows [isn0, isn1):
+// isum [M][isn1 - isn0][K/32]; y is not written.
+hipError_t launch_qmm_q8act(const void* W, const float* x, float* y, int32_t* isum, int64_t isn0, int64_t isn1,
+                            int64_t N, int64_t K, int64_t M, void* ws, hipStream_t stream);
 
 // Q4_0 x float32 activations (small M).  The workspace layout (and size)
 // depends on (N, K, M) only.

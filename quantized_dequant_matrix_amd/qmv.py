@@ -45,7 +45,7 @@ _SIGS = {
     "logits_topk": ([_P, _P, _P, _P, _I64, _I64, _I64, _I32, _F, _P, _SZ, _P], ctypes.c_int),
     "logits_sample": ([_P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I32, _F, _F, _F, _P, _SZ, _P], ctypes.c_int),
     "qmvdbg_quantize_q8": ([_P, _P, _P, _I64, _I64, _P], ctypes.c_int),
-    "qmvdbg_q4_0_q8_blocksums": ([_P, _P, _P, _I64, _I64, _I64, _P], ctypes.c_int),
+    "qmvdbg_qmm_q4_0_q8act_blocksums": ([_P, _P, _P, _I64, _I64, _I64, _I64, _I64, _P, _SZ, _P], ctypes.c_int),
     "qmvdbg_topk_f32": ([_P, _P, _P, _I64, _I64, _I32, _F, _P, _SZ, _P], ctypes.c_int),
     "qmvdbg_sample_f32": ([_P, _P, _P, _P, _P, _I64, _I32, _F, _F, _P], ctypes.c_int),
     "qmvdbg_stream_read": ([_P, _I64, _P, _I32, _P], ctypes.c_int),
@@ -162,8 +162,9 @@ def qmvdbg_quantize_q8(x, q, d, K, M, stream=None):
     _call("qmvdbg_quantize_q8", _ptr(x), _ptr(q), _ptr(d), K, M, _stream(stream))
 
 
-def qmvdbg_q4_0_q8_blocksums(W, qx, isum, N, K, M, stream=None):
-    _call("qmvdbg_q4_0_q8_blocksums", _ptr(W), _ptr(qx), _ptr(isum), N, K, M, _stream(stream))
+def qmvdbg_qmm_q4_0_q8act_blocksums(W, x, isum, N, K, M, n0, n1, ws, ws_bytes, stream=None):
+    _call("qmvdbg_qmm_q4_0_q8act_blocksums", _ptr(W), _ptr(x), _ptr(isum), N, K, M, n0, n1, _ptr(ws), ws_bytes,
+          _stream(stream))
 
 
 def qmvdbg_topk_f32(y, top_val, top_idx, N, M, k, softcap, ws, ws_bytes, stream=None):

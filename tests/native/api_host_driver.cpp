@@ -34,10 +34,8 @@ hipError_t launch_sample(const float*, const int32_t*, const float*, int32_t*, i
 size_t qmm_ws_bytes(int64_t N, int64_t K, int64_t M) { return static_cast<size_t>(M * K * 2 + N * M * 4 + 256); }
 hipError_t launch_quantize_q8(const float*, int8_t*, float*, int64_t K, int64_t M, hipStream_t) {
     rec(M, K); return hipSuccess; }
-hipError_t launch_qmm_q8act(const void*, const float*, float*, int64_t N, int64_t K, int64_t, void*, hipStream_t) {
-    rec(N, K); return hipSuccess; }
-hipError_t launch_q4_0_q8_blocksums(const void*, const int8_t*, int32_t*, int64_t N, int64_t K, int64_t,
-                                    hipStream_t) { rec(N, K); return hipSuccess; }
+hipError_t launch_qmm_q8act(const void*, const float*, float*, int32_t*, int64_t, int64_t, int64_t N, int64_t K,
+                            int64_t, void*, hipStream_t) { rec(N, K); return hipSuccess; }
 size_t qmm_f32act_ws_bytes(int64_t N, int64_t K, int64_t M) { return static_cast<size_t>(M * K * 4 + N * M * 4 + 256); }
 hipError_t launch_qmm_f32act(const void*, const float*, float*, int64_t N, int64_t K, int64_t, void*, hipStream_t) {
     rec(N, K); return hipSuccess; }
@@ -98,6 +96,13 @@ int main() {
     const size_t need = qmm_q4_0_q8act_ws_bytes(64, 256, 4);
     EXPECT(qmm_q4_0_q8act(W, x, y, 64, 256, 4, ws, need, s), QMV_OK);
     EXPECT(qmm_q4_0_q8act(W, x, y, 64, 256, 4, ws, need - 1, s), QMV_ERR_WORKSPACE);
+    EXPECT(qmvdbg_qmm_q4_0_q8act_blocksums(W, x, idx, 64, 256, 4, 8, 24, ws, need, s), QMV_OK);
+    EXPECT(qmvdbg_qmm_q4_0_q8act_blocksums(W, x, idx, 64, 256, 4, 8, 24, ws, need - 1, s), QMV_ERR_WORKSPACE);
+    EXPECT(qmvdbg_qmm_q4_0_q8act_blocksums(W, x, idx, 64, 256, 4, 8, 8, ws, need, s), QMV_ERR_ARG);
+    EXPECT(qmvdbg_qmm_q4_0_q8act_blocksums(W, x, idx, 64, 256, 4, -1, 8, ws, need, s), QMV_ERR_ARG);
+    EXPECT(qmvdbg_qmm_q4_0_q8act_blocksums(W, x, idx, 64, 256, 4, 0, 65, ws, need, s), QMV_ERR_ARG);
+    EXPECT(qmvdbg_qmm_q4_0_q8act_blocksums(W, x, nullptr, 64, 256, 4, 0, 8, ws, need, s), QMV_ERR_NULL);
+    EXPECT(qmvdbg_qmm_q4_0_q8act_blocksums(W, x, idx, 64, 256, 4, 0, 8, ws + 8, need, s), QMV_ERR_ALIGN);
     const size_t needf = qmm_q4_0_f32act_ws_bytes(64, 256, 4);
     EXPECT(qmm_q4_0_f32act(W, x, y, 64, 256, 4, ws, needf, s), QMV_OK);
     const size_t needt = logits_topk_ws_bytes(100, 2, 10);

@@ -230,7 +230,15 @@ def test_logits_sample_validation():
 def test_debug_entry_validation():
     assert call("qmvdbg_quantize_q8", FAKE, FAKE, FAKE, 40, 1, S) == SHAPE
     assert call("qmvdbg_quantize_q8", None, FAKE, FAKE, 64, 1, S) == NUL
-    assert call("qmvdbg_q4_0_q8_blocksums", FAKE, FAKE + 4, FAKE, 8, 64, 1, S) == ALIGN
+    bs = "qmvdbg_qmm_q4_0_q8act_blocksums"
+    assert call(bs, FAKE, FAKE + 2, FAKE, 8, 64, 1, 0, 8, FAKE, 1 << 20, S) == ALIGN
+    assert call(bs, FAKE, FAKE, FAKE, 8, 64, 1, 0, 8, FAKE + 8, 1 << 20, S) == ALIGN
+    assert call(bs, FAKE, FAKE, FAKE, 8, 64, 1, 4, 4, FAKE, 1 << 20, S) == ARG
+    assert call(bs, FAKE, FAKE, FAKE, 8, 64, 1, 0, 9, FAKE, 1 << 20, S) == ARG
+    assert call(bs, FAKE, FAKE, FAKE, 8, 64, 1, -1, 2, FAKE, 1 << 20, S) == ARG
+    assert call(bs, FAKE, FAKE, None, 8, 64, 1, 0, 8, FAKE, 1 << 20, S) == NUL
+    assert call(bs, FAKE, FAKE, FAKE, 8, 64, 1, 0, 8, FAKE, 16, S) == WS
+    assert call(bs, FAKE, FAKE, FAKE, 8, 48, 1, 0, 8, FAKE, 1 << 20, S) == SHAPE
     assert call("qmvdbg_topk_f32", FAKE, FAKE, FAKE, 100, 1, 101, 30.0, FAKE, 1 << 20, S) == ARG
 
 

@@ -26,11 +26,30 @@ def gpu_quantize(x, M, K):
     return host(q), host(d)
 
 
-def gpu_blocksums(W, qx, N, K, M):
+def gpu_blocksums(W, x, N, K, M, n0=0, n1=None):
+    """Block sums of rows n0..n1 from the launches qmm_q4_0_q8act makes for
+    (N, K, M): its quantizer, kernel and grid, the epilogue storing isum."""
     qmv = _qmv()
-    isum = empty((M, N, K // 32), dtype=torch.int32)
-    qmv.qmvdbg_q4_0_q8_blocksums(dev(W), dev(qx), isum, N, K, M)
+    n1 = N if n1 is None else n1
+    wsb = qmv.qmm_q4_0_q8act_ws_bytes(N, K, M)
+    ws = torch.empty(wsb, dtype=torch.uint8, device="cuda:0")
+    isum = empty((M, n1 - n0, K // 32), dtype=torch.int32)
+    qmv.qmvdbg_qmm_q4_0_q8act_blocksums(dev(W), dev(x), isum, N, K, M, n0, n1, ws, wsb)
     return host(isum)
+
+
+def ref_blocksums(W, x, N, K, M, n0=0, n1=None):
+    n1 = N if n1 is None else n1
+    qx, _ = oracle.quantize_q8(x, M, K)
+    return oracle.q4_0_q8_blocksums(W, N, K, qx, M, rows=np.arange(n0, n1))
+
+
+def qmm_path(N, K, M):
+    """The tiling qmm_q4_0_q8act picks for (N, K, M) (wide: 64 x 64 tiles,
+    at least 512 of them; narrow: 16 x 16 tiles; else the M = 1 kernels)."""
+    if M == 1 or K % 256:
+        return "dot"
+    return "wide" if -(-M // 64) * -(-N // 64) >= 512 else "narrow"
 
 
 def gpu_qmm(W, x, N, K, M):
@@ -68,25 +87,56 @@ def test_quantizer_ties_and_zero_blocks():
 
 
 @pytest.mark.parametrize("M", [1, 16, 512])
-def test_blocksums_bit_exact(M):
-    K = C4["K"]
-    n0, n = 1000, 96 if M < 512 else 24
-    say(f"qmvdbg_q4_0_q8_blocksums M={M} rows {n0}..{n0 + n}")
+@pytest.mark.parametrize("n0,n1", [(0, 128), (5248, 5376), (1000, 1100)])
+def test_blocksums_bit_exact(M, n0, n1):
+    """The C4 workload (N = 5376, K = 21504) at M = 1, 16 and 512: the block
+    sums of the kernel that computes y, bit for bit, on row ranges across
+    64-row tile edges (M = 512 takes the wide int8 MFMA tiling)."""
+    N, K = C4["N"], C4["K"]
+    assert qmm_path(N, K, M) == {1: "dot", 16: "narrow", 512: "wide"}[M]
+    say(f"qmvdbg_qmm_q4_0_q8act_blocksums c4 M={M} rows {n0}..{n1}")
     W, x = synth.config_problem("c4", M=M)
-    rb = oracle.row_bytes("q4_0", K)
-    Wsub = W[n0 * rb:(n0 + n) * rb]
-    qx, _ = oracle.quantize_q8(x, M, K)
-    got = gpu_blocksums(Wsub, qx, n, K, M)
-    ref = oracle.q4_0_q8_blocksums(Wsub, n, K, qx, M)
+    got = gpu_blocksums(W, x, N, K, M, n0, n1)
+    assert np.array_equal(got, ref_blocksums(W, x, N, K, M, n0, n1))
+
+
+@pytest.mark.parametrize("N,K,M", [(4160, 512, 520), (4160, 768, 520), (8200, 256, 512)])
+def test_blocksums_wide_ragged(N, K, M):
+    """The wide tiling on every row, with M off the 64-row tiles, N on and off
+    them, and K / 32 = 16, 24 and 8 blocks (whole and half weight chunks)."""
+    assert qmm_path(N, K, M) == "wide"
+    say(f"qmvdbg_qmm_q4_0_q8act_blocksums wide N={N} K={K} M={M}")
+    W, x = synth.problem("q4_0", N, K, M, 11 * N + K + M)
+    assert np.array_equal(gpu_blocksums(W, x, N, K, M), ref_blocksums(W, x, N, K, M))
+
+
+def test_blocksums_wide_extreme_codes():
+    """Blocks at the integer extremes on the wide tiling: codes +-127 against
+    weight rows of all q_w = 0 and all q_w = 15 (block sums +-32512 and
+    +-28448), and random mixtures of the extremes."""
+    N, K, M = 4096, 256, 512
+    assert qmm_path(N, K, M) == "wide"
+    say("qmvdbg_qmm_q4_0_q8act_blocksums wide, extreme codes")
+    rng = np.random.default_rng(21)
+    q = np.where(rng.random((N, K // 32, 32)) < 0.5, 0, 15).astype(np.uint8)
+    q[0], q[1] = 0, 15
+    W = synth.pack_q4_0(np.ones(N * K // 32, np.float16), q.reshape(-1, 32))
+    x = np.where(rng.random((M, K)) < 0.5, -3.0, 3.0).astype(np.float32)
+    x[:128], x[128:256] = 3.0, -3.0
+    got = gpu_blocksums(W, x, N, K, M)
+    ref = ref_blocksums(W, x, N, K, M)
+    assert ref.min() == -32512 and ref.max() == 32512
+    assert set(np.unique(ref[:256, :2])) == {-32512, -28448, 28448, 32512}
     assert np.array_equal(got, ref)
 
 
-@pytest.mark.parametrize("N,K,M", [(5, 64, 1), (70, 256, 3), (33, 5408, 2), (129, 4096, 16), (64, 2048, 40)])
-def test_blocksums_shapes(N, K, M):
-    say(f"qmvdbg_q4_0_q8_blocksums N={N} K={K} M={M}")
+@pytest.mark.parametrize("N,K,M,n0,n1", [(5, 64, 1, 0, 5), (70, 256, 3, 3, 69), (33, 5408, 2, 0, 33),
+                                         (129, 4096, 16, 64, 129), (64, 2048, 40, 0, 64), (200, 512, 1, 7, 9),
+                                         (300, 16640, 5, 250, 300)])
+def test_blocksums_shapes(N, K, M, n0, n1):
+    say(f"qmvdbg_qmm_q4_0_q8act_blocksums N={N} K={K} M={M} rows {n0}..{n1} ({qmm_path(N, K, M)})")
     W, x = synth.problem("q4_0", N, K, M, N * M + K)
-    qx, _ = oracle.quantize_q8(x, M, K)
-    assert np.array_equal(gpu_blocksums(W, qx, N, K, M), oracle.q4_0_q8_blocksums(W, N, K, qx, M))
+    assert np.array_equal(gpu_blocksums(W, x, N, K, M, n0, n1), ref_blocksums(W, x, N, K, M, n0, n1))
 
 
 def _qmm_ref(W, x, N, K, M, rows=None):
@@ -105,15 +155,15 @@ def test_qmm_workload_full(M):
     say(f"c4 M={M}: worst err/tol {w:.3g}")
 
 
-def test_qmm_workload_m512_sampled():
+def test_qmm_workload_m512_full():
+    """The C4 workload at M = 512 (the wide int8 MFMA tiling) on all 5376 rows."""
     N, K, M = C4["N"], C4["K"], 512
-    say("qmm_q4_0_q8act workload M=512, 48 sampled rows")
+    assert qmm_path(N, K, M) == "wide"
+    say("qmm_q4_0_q8act workload M=512, all rows")
     W, x = synth.config_problem("c4", M=M)
     y = gpu_qmm(W, x, N, K, M)
-    rows = np.sort(np.random.default_rng(4).choice(N, 48, replace=False))
-    yr, S = _qmm_ref(W, x, N, K, M, rows=rows)
-    w = assert_within(y[:, rows], yr, oracle.float_tol(S), "c4 M=512")
-    assert np.all(np.isfinite(y))
+    yr, S = _qmm_ref(W, x, N, K, M)
+    w = assert_within(y, yr, oracle.float_tol(S), "c4 M=512")
     say(f"c4 M=512: worst err/tol {w:.3g}")
 
 
@@ -140,10 +190,14 @@ def test_qmm_shapes(N, K, M):
     assert_within(y, yr, oracle.float_tol(S), "qmm")
 
 
-def test_qmm_integer_valued_is_exact():
-    say("qmm_q4_0_q8act integer-valued case")
-    rng = np.random.default_rng(8)
-    N, K, M = 300, 21504, 16
+@pytest.mark.parametrize("N,K,M", [(300, 21504, 16), (4096, 2048, 512)])
+def test_qmm_integer_valued_is_exact(N, K, M):
+    """Unit weight scales and one 127 in every activation block (d_x = 1):
+    y is the integer sum of the block sums, below 2^24 in every partial sum,
+    so it must be exact in any order -- on the narrow (M = 16) and the wide
+    (M = 512) int8 MFMA tilings."""
+    say(f"qmm_q4_0_q8act integer-valued case N={N} K={K} M={M} ({qmm_path(N, K, M)})")
+    rng = np.random.default_rng(8 + M)
     q = rng.integers(0, 16, size=(N * K // 32, 32), dtype=np.uint8)
     W = synth.pack_q4_0(np.ones(N * K // 32, np.float16), q)
     x = rng.integers(-64, 65, size=(M, K)).astype(np.float32)
