@@ -223,6 +223,25 @@ int logits_topk(const void* W_q8_0, const float* x, float* top_val, int32_t* top
                 int64_t N, int64_t K, int64_t M, int32_t k, float softcap,
                 void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* logits_topk for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same computation, kernels and results, with the workspace taken from
+ * a fixed device array inside the library instead of a caller's buffer.
+ * The array holds QMV_STATIC_SCRATCH_BYTES (8 MiB); each GPU that runs the
+ * library has its own copy, kept until the process ends.  A call needs
+ * logits_topk_ws_bytes(N, M, k) <= QMV_STATIC_SCRATCH_BYTES (a 262,144-entry
+ * vocabulary: up to 7 rows at k = 10, 5 at k = 64), else it returns
+ * QMV_ERR_WORKSPACE and launches nothing; QMV_ERR_LAUNCH also if the runtime
+ * cannot give the array's address.  No call allocates or frees memory.
+ * Every call on one GPU uses that GPU's one array: calls that overlap in
+ * time on one GPU (on different streams, or from different host threads)
+ * race and must be ordered by the caller.  Nothing in the array needs to
+ * start at zero (each call writes every byte it reads), and it keeps the last
+ * call's logits until the next call. */
+#define QMV_STATIC_SCRATCH_BYTES ((size_t)8 << 20)
+int logits_topk_noalloc(const void* W_q8_0, const float* x, float* top_val, int32_t* top_idx,
+                        int64_t N, int64_t K, int64_t M, int32_t k, float softcap, hipStream_t stream);
+
 /* Token selection on the device after the logit projection: logits_topk,
  * then one draw per row from the k selected pairs.
  *   w_i = exp((top_val[m][i] - top_val[m][0]) / temperature), i < k

@@ -11,6 +11,8 @@
 
 #include "qmv_internal.h"
 
+static_assert(qmv::kStaticScratchBytes == QMV_STATIC_SCRATCH_BYTES, "one size for the static workspace");
+
 namespace {
 
 constexpr int64_t kMaxN = (int64_t{1} << 31) - 1;
@@ -188,16 +190,25 @@ size_t logits_topk_ws_bytes(int64_t N, int64_t M, int32_t k) {
     return qmv::topk_ws_bytes(N, M, k);
 }
 
-static int check_topk_args(int64_t N, int64_t M, int32_t k, float softcap, const float* top_val,
-                           const int32_t* top_idx, void* ws, size_t ws_bytes) {
-    if (!top_val || !top_idx || !ws) return QMV_ERR_NULL;
+// k, the cap and the outputs of a top-k call; then the workspace it needs
+static int check_topk_params(int64_t N, int64_t M, int32_t k, float softcap, const float* top_val,
+                             const int32_t* top_idx) {
+    if (!top_val || !top_idx) return QMV_ERR_NULL;
     if (M > 65535) return QMV_ERR_SHAPE;
     if (k < 1 || k > 64 || k > N) return QMV_ERR_ARG;
     if (!(softcap > 0.0f) || !(softcap <= 3.4028234663852886e38f)) return QMV_ERR_ARG;
-    if (!aligned(top_val, 4) || !aligned(top_idx, 4) || !aligned(ws, 16)) return QMV_ERR_ALIGN;
-    const size_t need = logits_topk_ws_bytes(N, M, k);
-    if (need == 0) return QMV_ERR_SHAPE;
-    if (ws_bytes < need) return QMV_ERR_WORKSPACE;
+    if (!aligned(top_val, 4) || !aligned(top_idx, 4)) return QMV_ERR_ALIGN;
+    if (logits_topk_ws_bytes(N, M, k) == 0) return QMV_ERR_SHAPE;
+    return QMV_OK;
+}
+
+static int check_topk_args(int64_t N, int64_t M, int32_t k, float softcap, const float* top_val,
+                           const int32_t* top_idx, void* ws, size_t ws_bytes) {
+    if (!ws) return QMV_ERR_NULL;
+    const int rc = check_topk_params(N, M, k, softcap, top_val, top_idx);
+    if (rc) return rc;
+    if (!aligned(ws, 16)) return QMV_ERR_ALIGN;
+    if (ws_bytes < logits_topk_ws_bytes(N, M, k)) return QMV_ERR_WORKSPACE;
     return QMV_OK;
 }
 
@@ -215,6 +226,22 @@ int logits_topk(const void* W_q8_0, const float* x, float* top_val, int32_t* top
         if (rc) return rc;
     }
     return launched(qmv::launch_topk(y, top_val, top_idx, N, M, k, softcap, ws, stream));
+}
+
+int logits_topk_noalloc(const void* W_q8_0, const float* x, float* top_val, int32_t* top_idx, int64_t N, int64_t K,
+                        int64_t M, int32_t k, float softcap, hipStream_t stream) {
+    // every check (the static workspace's size included) comes before the
+    // runtime is asked for the workspace's address
+    if (!W_q8_0 || !x) return QMV_ERR_NULL;
+    int rc = check_shape(N, K, M, 32, 34);
+    if (rc) return rc;
+    rc = check_topk_params(N, M, k, softcap, top_val, top_idx);
+    if (rc) return rc;
+    if (logits_topk_ws_bytes(N, M, k) > qmv::kStaticScratchBytes) return QMV_ERR_WORKSPACE;
+    if (!aligned(W_q8_0, 16) || !aligned(x, 4)) return QMV_ERR_ALIGN;
+    void* ws = qmv::static_scratch();
+    if (!ws) return QMV_ERR_LAUNCH;
+    return logits_topk(W_q8_0, x, top_val, top_idx, N, K, M, k, softcap, ws, qmv::kStaticScratchBytes, stream);
 }
 
 static int check_sample_args(const float* u, const int32_t* token, const int32_t* nucleus, float temperature,

@@ -36,6 +36,13 @@ size_t topk_ws_bytes(int64_t N, int64_t M, int k);
 hipError_t launch_topk(const float* y, float* top_val, int32_t* top_idx, int64_t N, int64_t M,
                        int k, float softcap, void* ws, hipStream_t stream);
 
+// The workspace of logits_topk_noalloc: a device array of this many bytes,
+// one per GPU, never allocated or freed by a call.  static_scratch() gives
+// the current device's copy (its address is looked up once per device), or
+// nullptr if the runtime cannot name it.
+constexpr size_t kStaticScratchBytes = size_t{8} << 20;
+void* static_scratch();
+
 // One token per row from the k selected pairs (top-p with temperature, the
 // caller's uniform numbers u[M]).
 hipError_t launch_sample(const float* top_val, const int32_t* top_idx, const float* u, int32_t* token,

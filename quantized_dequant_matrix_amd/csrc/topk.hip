@@ -37,6 +37,8 @@
 // fall back to a merge that rescans candidates from memory every round.
 #include <stdint.h>
 
+#include <mutex>
+
 #include "qmv_device.h"
 #include "qmv_internal.h"
 
@@ -583,6 +585,31 @@ hipError_t launch_topk(const float* y, float* top_val, int32_t* top_idx, int64_t
                            y, N, k, nwchunks, softcap, cand, top_val, top_idx);
     }
     return hipGetLastError();
+}
+
+// Workspace of logits_topk_noalloc, for callers that cannot allocate: a
+// file-scope device array of kStaticScratchBytes, one copy per GPU (each
+// device that loads the library holds its own until the process ends).  Host
+// code never uses the array's name as an address: that is a host-side
+// stand-in.  static_scratch() asks the runtime for the device address of the
+// current device's copy once per device and hands that out.
+namespace {
+__device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+}  // namespace
+
+void* static_scratch() {
+    constexpr int kMaxDevices = 64;
+    static std::mutex mu;
+    static void* ptr[kMaxDevices] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    std::lock_guard<std::mutex> lock(mu);
+    if (ptr[dev] == nullptr) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+        ptr[dev] = p;
+    }
+    return ptr[dev];
 }
 
 hipError_t launch_sample(const float* top_val, const int32_t* top_idx, const float* u, int32_t* token,

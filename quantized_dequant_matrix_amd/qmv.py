@@ -43,6 +43,7 @@ _SIGS = {
     "qmm_q4_0_f32act": ([_P, _P, _P, _I64, _I64, _I64, _P, _SZ, _P], ctypes.c_int),
     "logits_topk_ws_bytes": ([_I64, _I64, _I32], _SZ),
     "logits_topk": ([_P, _P, _P, _P, _I64, _I64, _I64, _I32, _F, _P, _SZ, _P], ctypes.c_int),
+    "logits_topk_noalloc": ([_P, _P, _P, _P, _I64, _I64, _I64, _I32, _F, _P], ctypes.c_int),
     "logits_sample": ([_P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I32, _F, _F, _F, _P, _SZ, _P], ctypes.c_int),
     "qmvdbg_quantize_q8": ([_P, _P, _P, _I64, _I64, _P], ctypes.c_int),
     "qmvdbg_qmm_q4_0_q8act_blocksums": ([_P, _P, _P, _I64, _I64, _I64, _I64, _I64, _P, _SZ, _P], ctypes.c_int),
@@ -156,6 +157,11 @@ def logits_topk_ws_bytes(N, M, k) -> int:
 def logits_topk(W_q8_0, x, top_val, top_idx, N, K, M, k, softcap, ws, ws_bytes, stream=None):
     _call("logits_topk", _ptr(W_q8_0), _ptr(x), _ptr(top_val), _ptr(top_idx), N, K, M, k, softcap,
           _ptr(ws), ws_bytes, _stream(stream))
+
+
+def logits_topk_noalloc(W_q8_0, x, top_val, top_idx, N, K, M, k, softcap, stream=None):
+    _call("logits_topk_noalloc", _ptr(W_q8_0), _ptr(x), _ptr(top_val), _ptr(top_idx), N, K, M, k, softcap,
+          _stream(stream))
 
 
 def qmvdbg_quantize_q8(x, q, d, K, M, stream=None):

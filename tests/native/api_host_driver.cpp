@@ -29,6 +29,7 @@ hipError_t launch_qkv(const void*, const void*, const void*, const float*, float
 size_t topk_ws_bytes(int64_t N, int64_t M, int k) { return static_cast<size_t>(N * M * 4 + M * k * 8 * 64); }
 hipError_t launch_topk(const float*, float*, int32_t*, int64_t N, int64_t, int, float, void*, hipStream_t) {
     rec(N, 0); return hipSuccess; }
+void* static_scratch() { alignas(256) static unsigned char buf[4096]; return buf; }
 hipError_t launch_sample(const float*, const int32_t*, const float*, int32_t*, int32_t*, int64_t M, int k, float,
                          float, hipStream_t) { rec(M, k); return hipSuccess; }
 size_t qmm_ws_bytes(int64_t N, int64_t K, int64_t M) { return static_cast<size_t>(M * K * 2 + N * M * 4 + 256); }
@@ -96,6 +97,12 @@ int main() {
     const size_t need = qmm_q4_0_q8act_ws_bytes(64, 256, 4);
     EXPECT(qmm_q4_0_q8act(W, x, y, 64, 256, 4, ws, need, s), QMV_OK);
     EXPECT(qmm_q4_0_q8act(W, x, y, 64, 256, 4, ws, need - 1, s), QMV_ERR_WORKSPACE);
+    g_calls = 0;
+    EXPECT(logits_topk_noalloc(W, x, y, idx, 100, 64, 2, 10, 30.0f, s), QMV_OK);
+    if (g_calls != 3 || g_N != 100) { std::fprintf(stderr, "noalloc top-k launches\n"); ++failures; }
+    EXPECT(logits_topk_noalloc(W, x, y, idx, 262144, 64, 8, 10, 30.0f, s), QMV_ERR_WORKSPACE);
+    EXPECT(logits_topk_noalloc(W, x, y, idx, big, 64, 8, 10, 30.0f, s), QMV_ERR_SHAPE);
+    EXPECT(logits_topk_noalloc(W, x, y, idx, 100, 64, 1, 0, 30.0f, s), QMV_ERR_ARG);
     EXPECT(qmvdbg_qmm_q4_0_q8act_blocksums(W, x, idx, 64, 256, 4, 8, 24, ws, need, s), QMV_OK);
     EXPECT(qmvdbg_qmm_q4_0_q8act_blocksums(W, x, idx, 64, 256, 4, 8, 24, ws, need - 1, s), QMV_ERR_WORKSPACE);
     EXPECT(qmvdbg_qmm_q4_0_q8act_blocksums(W, x, idx, 64, 256, 4, 8, 8, ws, need, s), QMV_ERR_ARG);

@@ -26,7 +26,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported_and_bound():
     names = declared_functions()
-    assert "qmv_q4_0" in names and "logits_topk" in names and len(names) == 23
+    assert "qmv_q4_0" in names and "logits_topk" in names and len(names) == 24
     for n in names:
         assert hasattr(qmv.lib, n), n
     assert sorted(qmv.EXPORTS) == names
@@ -240,6 +240,25 @@ def test_debug_entry_validation():
     assert call(bs, FAKE, FAKE, FAKE, 8, 64, 1, 0, 8, FAKE, 16, S) == WS
     assert call(bs, FAKE, FAKE, FAKE, 8, 48, 1, 0, 8, FAKE, 1 << 20, S) == SHAPE
     assert call("qmvdbg_topk_f32", FAKE, FAKE, FAKE, 100, 1, 101, 30.0, FAKE, 1 << 20, S) == ARG
+
+
+def test_noalloc_topk_validation():
+    """logits_topk_noalloc rejects, before it asks the runtime for its static
+    workspace, every request that logits_topk would reject and every one
+    whose workspace exceeds the 8 MiB static array."""
+    f = "logits_topk_noalloc"
+    assert call(f, None, FAKE, FAKE, FAKE, 1000, 64, 1, 10, 30.0, S) == NUL
+    assert call(f, FAKE, FAKE, None, FAKE, 1000, 64, 1, 10, 30.0, S) == NUL
+    assert call(f, FAKE, FAKE, FAKE, FAKE, 1000, 48, 1, 10, 30.0, S) == SHAPE
+    assert call(f, FAKE, FAKE, FAKE, FAKE, 1000, 64, 1, 65, 30.0, S) == ARG
+    assert call(f, FAKE, FAKE, FAKE, FAKE, 1000, 64, 1, 10, 0.0, S) == ARG
+    assert call(f, FAKE + 8, FAKE, FAKE, FAKE, 1000, 64, 1, 10, 30.0, S) == ALIGN
+    assert call(f, FAKE, FAKE, FAKE + 2, FAKE, 1000, 64, 1, 10, 30.0, S) == ALIGN
+    # 262,144 logits: 7 rows fit at k = 10, 8 do not; 5 fit at k = 64, 6 do not
+    assert qmv.logits_topk_ws_bytes(262144, 7, 10) <= 8 << 20 < qmv.logits_topk_ws_bytes(262144, 8, 10)
+    assert qmv.logits_topk_ws_bytes(262144, 5, 64) <= 8 << 20 < qmv.logits_topk_ws_bytes(262144, 6, 64)
+    assert call(f, FAKE, FAKE, FAKE, FAKE, 262144, 64, 8, 10, 30.0, S) == WS
+    assert call(f, FAKE, FAKE, FAKE, FAKE, 262144, 64, 6, 64, 30.0, S) == WS
 
 
 def test_stream_read_validation():
