@@ -49,13 +49,37 @@ struct FragLayout {
     }
 };
 
-// One 8-lane group per 32-element block, 4 elements per lane.  FRAG: write
-// the fragment layout (rows padded to a multiple of 16), else row-major
-// codes [M][K] and scales [M][K/32].
-template <bool FRAG>
+// The scale d_x of a block as three bfloat16 terms, d_x = h + m + l exactly
+// (each a truncation of what is left: 8 + 8 + 8 significant bits cover the
+// 24 of a float32; only parts below the bfloat16 range, under 2^-133, are
+// lost).  The wide MFMA kernel forms the products d_w * d_x with a
+// bfloat16 MFMA from these terms.  Returned as the 16-byte operand pair
+// (h, m, l, h | m, l, 0, 0): k-half 0 and k-half 1 of that MFMA's A operand.
+__device__ __forceinline__ uint4 bf16_split3(float v) {
+    const uint32_t h = __float_as_uint(v) & 0xffff0000u;
+    const float r1 = v - __uint_as_float(h);
+    const uint32_t m = __float_as_uint(r1) & 0xffff0000u;
+    const uint32_t l = __float_as_uint(r1 - __uint_as_float(m)) & 0xffff0000u;
+    return make_uint4((h >> 16) | m, (l >> 16) | h, (m >> 16) | l, 0u);
+}
+
+// Layouts of the quantized activations in the workspace.
+//   kLayoutRows:  codes [M][K], scales float [M][K/32] (M == 1, the export).
+//   kLayoutFrag:  the fragment layout above (narrow MFMA tiling).
+//   kLayoutSplit: (wide MFMA tiling) tiles of 32 rows, Mt = Mrows / 32:
+//                 codes [Mt][K/32][64 lanes][16 B], lane l = i + 32 h holding
+//                 elements 16 h .. 16 h + 15 of row 32 t + i; scales as
+//                 bf16_split3 operands, uint4 [Mt][K/32][32] (row 32 t + i).
+//                 One wave's operand of a block is 1 KB contiguous.
+// Rows M .. Mrows - 1 are quantized as zeros.
+enum QLayout : int { kLayoutRows = 0, kLayoutFrag = 1, kLayoutSplit = 2 };
+
+// One 8-lane group per 32-element block, 4 elements per lane.
+template <int LAYOUT>
 __global__ __launch_bounds__(kBlockThreads)
 void quantize_q8_kernel(const float* __restrict__ x, int8_t* __restrict__ q, float* __restrict__ d,
                         int64_t K, int64_t M, int64_t Mrows, bool vec_x, bool vec_q) {
+    static_assert(LAYOUT == kLayoutRows || LAYOUT == kLayoutFrag, "kLayoutSplit: quantize_q8_tiles_kernel");
     const int64_t nb = K / 32;
     const int64_t total = Mrows * nb;  // blocks, padding rows included
     const int t = threadIdx.x & 7;
@@ -94,7 +118,7 @@ void quantize_q8_kernel(const float* __restrict__ x, int8_t* __restrict__ q, flo
             packed |= (static_cast<uint32_t>(qv) & 0xffu) << (8 * e);
         }
         if (ok) {
-            if constexpr (FRAG) {
+            if constexpr (LAYOUT == kLayoutFrag) {
                 const FragLayout L{nb};
                 reinterpret_cast<uint32_t*>(q)[L.code_dword(m, b, t)] = packed;
                 if (t == 0) d[L.scale_index(m, b)] = db;
@@ -109,6 +133,60 @@ void quantize_q8_kernel(const float* __restrict__ x, int8_t* __restrict__ q, flo
                 if (t == 0) d[m * nb + b] = db;
             }
         }
+    }
+}
+
+// kLayoutSplit: one wave per (32-row tile, block); lane l = i + 32 h
+// quantizes elements 16 h .. 16 h + 15 of row 32 t + i (the block's amax
+// joins the two halves with one exchange) and writes its 16 code bytes where
+// the wide kernel's lane l reads them: each wave writes 1 KB contiguous.
+// The arithmetic is quantize_q8_kernel's, element for element.
+__global__ __launch_bounds__(kBlockThreads)
+void quantize_q8_tiles_kernel(const float* __restrict__ x, int8_t* __restrict__ q, uint4* __restrict__ ds,
+                              int64_t K, int64_t M, int64_t Mrows, bool vec_x) {
+    const int64_t nb = K / 32;
+    const int64_t items = (Mrows / 32) * nb;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int i = lane & 31, h = lane >> 5;
+    const int64_t stride = static_cast<int64_t>(gridDim.x) * kWavesPerBlock;
+    for (int64_t it = static_cast<int64_t>(blockIdx.x) * kWavesPerBlock + threadIdx.x / kWave; it < items;
+         it += stride) {
+        const int64_t mt = it / nb, b = it - mt * nb;
+        const int64_t m = mt * 32 + i;
+        float v[16];
+#pragma unroll
+        for (int e = 0; e < 16; ++e) v[e] = 0.0f;
+        if (m < M) {
+            const float* src = x + m * K + 32 * b + 16 * h;
+            if (vec_x) {
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    const float4 f = reinterpret_cast<const float4*>(src)[c];
+                    v[4 * c] = f.x; v[4 * c + 1] = f.y; v[4 * c + 2] = f.z; v[4 * c + 3] = f.w;
+                }
+            } else {
+#pragma unroll
+                for (int e = 0; e < 16; ++e) v[e] = src[e];
+            }
+        }
+        float a = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) a = fmaxf(a, fabsf(v[e]));
+        a = fmaxf(a, __shfl_xor(a, 32, kWave));
+        const float db = a / 127.0f;
+        uint32_t packed[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            int qv = 0;
+            if (a != 0.0f) {
+                float r = roundf(v[e] / db);
+                r = fminf(fmaxf(r, -127.0f), 127.0f);
+                qv = static_cast<int>(r);
+            }
+            packed[e / 4] |= (static_cast<uint32_t>(qv) & 0xffu) << (8 * (e % 4));
+        }
+        reinterpret_cast<uint4*>(q)[it * kWave + lane] = make_uint4(packed[0], packed[1], packed[2], packed[3]);
+        if (h == 0) ds[it * 32 + i] = bf16_split3(db);
     }
 }
 
@@ -501,41 +579,55 @@ void qmm_mfma_kernel(const uint8_t* __restrict__ W, const int8_t* __restrict__ x
     }
 }
 
-// The wide tiling (M = 512 class), with the weight codes decoded once per
-// workgroup.  A 64 x 64 tile per workgroup, 32 x 32 per wave (2 x 2 MFMA tiles
-// of 16 x 16).  Per chunk of KC = 16 blocks:
-//   * weights: a thread owns 4 whole blocks (72 bytes) of one of the 64 rows,
-//     fetched with 8-byte loads one chunk ahead, decoded in registers to
-//     16 (q - 8) signed bytes and d / 16, and stored in LDS in the MFMA
-//     operand layout: block j, k-group g, row r at
-//     bq[j * kBlockStride + g * kGroupStride + 2 r] (8 bytes).  The group
-//     stride puts a wave's four k-group reads on bank halves two by two, the
-//     block stride puts the four quarter-row writers of a wave on disjoint
-//     banks;
-//   * activations: read from the fragment layout in global memory (the
-//     whole [M, K] set stays in the caches), one block pair ahead of the
-//     multiplies, with unconditional loads so that no branch merges the
-//     waits (the pair after the last one re-reads the last pair).
+// The wide tiling (M = 512 class): 64 x 64 outputs per workgroup, four waves
+// as 2 (halves of the 64 activation rows) x 2 (even and odd blocks of each
+// chunk), each wave a 32 x 64 tile = two 32 x 32 MFMA tiles.
 //
-// MODE kModeISum replaces the float epilogue by a store of the exact block
-// sums of the rows n in [isn0, isn1) (isum [M][isn1 - isn0][nb]); every other
-// step -- the grid, the weight stash and decode, the operand layouts and the
-// MFMAs -- is the one that computes y.
-template <int KC, int MODE>
+// v_mfma_i32_32x32x32_i8 covers exactly one block: A 32 x 32 (lane l: row
+// l % 32, elements 16 (l / 32) .. + 15 of the block), B 32 x 32 (lane l:
+// column l % 32, the same 16 elements), D 32 x 32 int32 (lane l: column
+// l % 32, rows 8 (i / 4) + 4 (l / 32) + i % 4 for i < 16).  A and B take the
+// same element at the same byte of the same lane half, so D is the block's
+// integer sum whatever order the hardware adds in.
+//   * Activations: the tile-major layout (kLayoutSplit), a wave's operand of
+//     a block is one coalesced 1 KB load, from global memory, three of the
+//     wave's blocks ahead.
+//   * Weights: 64 rows x 16 blocks per chunk, fetched one chunk ahead into
+//     registers (whole block pairs, eight lanes per row), decoded
+//     once per workgroup into LDS planes [block][half][row][16 B] of
+//     16 (q - 8) signed bytes (half 0: low nibbles = elements 0 .. 15, half
+//     1: high nibbles = elements 16 .. 31), so the integer sums are 16 isum.
+//   * Scales: the product d_w * d_x / 16 of every (row, column) of a block
+//     comes from one v_mfma_f32_32x32x8_bf16 (the same D layout) over the
+//     exact bfloat16 terms of both scales: A = (h, m, l, h | m, l, 0, 0) of
+//     d_x (bf16_split3), B = (H, H, H, L | L, L, 0, 0) of d_w / 16 = H + L
+//     (11 significant bits: 8 + 3), so the six products h H + m H + l H +
+//     h L + m L + l L are exact and summed in float32.  The epilogue is then
+//     one convert and one FMA per output and block: acc += float(D) * S.
+// The two waves of a row half add their sums in LDS at the end, even blocks
+// first.  MODE kModeISum stores the block sums D / 16 of rows n in
+// [isn0, isn1) instead (isum [M][isn1 - isn0][nb]), with every other step
+// unchanged.
+typedef int v16i __attribute__((ext_vector_type(16)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef short s4 __attribute__((ext_vector_type(4)));
+
+template <int MODE>
 __global__ __launch_bounds__(kBlockThreads)
-void qmm_wide_kernel(const uint8_t* __restrict__ W, const int8_t* __restrict__ xa, const float* __restrict__ xd,
+void qmm_wide_kernel(const uint8_t* __restrict__ W, const int8_t* __restrict__ xq, const uint4* __restrict__ xs,
                      float* __restrict__ out, int32_t* __restrict__ isum, int N, int64_t M, int nb, int64_t tm0,
                      int64_t tiles_m, int tiles_n, int64_t nwg, int isn0, int isn1) {
     static_assert(MODE == kModeY || MODE == kModeISum, "y or block sums");
-    constexpr int MW = 2, NW = 2, WM = 2, WN = 2;
-    constexpr int TN = 16 * NW * WN;           // 64 weight rows
-    constexpr int kGroupStride = 2 * TN + 32;  // dwords: k-groups 32 banks apart
-    constexpr int kBlockStride = 4 * kGroupStride + 4;
-    static_assert(TN * 4 == kBlockThreads, "a thread owns one quarter of a row's chunk");
-    static_assert(KC == 16, "four quarters of four blocks per row");
-    static_assert(WM * WN == kWavesPerBlock, "four waves per workgroup");
-    __shared__ __align__(16) uint32_t bq[KC * kBlockStride];
-    __shared__ float bs[KC * TN];
+    constexpr int TM = 64, TN = 64, KC = 16;
+    // LDS planes, [block j][half g] each TN rows of 16 (or 8) bytes.  The
+    // stride of a block's plane pair is odd in 16-byte (8-byte) units, so
+    // that the eight lanes that stash the eight block pairs of one row, and
+    // the rows next to them, write to different banks.
+    constexpr int kQStride = 2 * TN + 1;  // uint4 per block j
+    constexpr int kSStride = 2 * TN + 1;  // uint2 per block j
+    static_assert(kWavesPerBlock == 4 && KC == 16, "two block pairs of 32 rows per thread");
+    __shared__ __align__(16) uint4 bq[KC * kQStride];   // decoded codes, 32.3 KB
+    __shared__ __align__(16) uint2 bsc[KC * kSStride];  // scale operands, 16.1 KB
 
     // Each XCD gets a contiguous run of tiles (same weight rows, all m-tiles).
     int64_t lin = blockIdx.x;
@@ -547,155 +639,167 @@ void qmm_wide_kernel(const uint8_t* __restrict__ W, const int8_t* __restrict__ x
 
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int lane = threadIdx.x & (kWave - 1);
-    const int wn = w % WN;
-    const int wm = w / WN;
-    const int li = lane & 15;
-    const int lg = lane >> 4;
+    const int wm = w & 1;      // activation rows 32 wm .. 32 wm + 31 of the tile
+    const int wk = w >> 1;     // blocks wk, wk + 2, ... of each chunk
+    const int li = lane & 31;  // A row / B column of the lane
+    const int lg = lane >> 5;  // k half of the lane
 
-    // Weight chunk: thread -> row fr, quarter fq = blocks 4 fq .. 4 fq + 3.
-    // nb is a multiple of 8, so a quarter is either whole or past the end;
-    // quarters past the end (and rows past N) read valid bytes that are never
-    // used.  Rows are 16-byte aligned (nb * 18 = 144 * (nb / 8)).
-    const int fr = threadIdx.x >> 2;
-    const int fq = threadIdx.x & 3;
-    const uint8_t* frow = W + static_cast<int64_t>(min(n0 + fr, N - 1)) * row_bytes;
-    uint2 raw[9];
+    // Weight chunk (64 rows x 16 blocks): thread t fetches block pair
+    // fp = t % 8 (36 bytes, 4-byte aligned) of rows fr = t / 8 and fr + 32,
+    // so that eight consecutive lanes read a row's 288 bytes.  A last chunk
+    // of 8 blocks reads (unused) pairs 0 .. 3 again; rows past N read row
+    // N - 1.
+    const int fp = threadIdx.x & 7;
+    const int fr = threadIdx.x >> 3;
+    const uint8_t* frow0 = W + static_cast<int64_t>(min(n0 + fr, N - 1)) * row_bytes;
+    const uint8_t* frow1 = W + static_cast<int64_t>(min(n0 + fr + 32, N - 1)) * row_bytes;
+    uint32_t raw[2][9];
     auto fetch = [&](int c0) {
-        const int b0 = c0 + 4 * fq;
-        const int64_t off = (b0 < nb) ? static_cast<int64_t>(b0) * 18 : 0;
-        const uint2* src = reinterpret_cast<const uint2*>(frow + off);
+        const int b0 = c0 + 2 * fp;
+        const int64_t off = static_cast<int64_t>(b0 < nb ? b0 : c0) * 18;
 #pragma unroll
-        for (int i = 0; i < 9; ++i) raw[i] = src[i];
+        for (int h = 0; h < 2; ++h) {
+            const uint8_t* src = (h ? frow1 : frow0) + off;
+            const u32x4_a4 a = *reinterpret_cast<const u32x4_a4*>(src);
+            const u32x4_a4 b = *reinterpret_cast<const u32x4_a4*>(src + 16);
+            raw[h][0] = a.x; raw[h][1] = a.y; raw[h][2] = a.z; raw[h][3] = a.w;
+            raw[h][4] = b.x; raw[h][5] = b.y; raw[h][6] = b.z; raw[h][7] = b.w;
+            raw[h][8] = *reinterpret_cast<const uint32_t*>(src + 32);
+        }
     };
     auto stash = [&]() {
-        uint32_t dw[18];
 #pragma unroll
-        for (int i = 0; i < 9; ++i) {
-            dw[2 * i] = raw[i].x;
-            dw[2 * i + 1] = raw[i].y;
-        }
+        for (int h = 0; h < 2; ++h) {
+            const int row = fr + 32 * h;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int blk = 4 * fq + j;
-            uint32_t dbits, code[4];
-            if ((j & 1) == 0) {  // block starts on a dword: codes 2 bytes in
-                const int q0 = (18 * j) / 4;
-                dbits = dw[q0] & 0xffffu;
+            for (int e = 0; e < 2; ++e) {
+                const int j = 2 * fp + e;
+                uint32_t dbits, code[4];
+                if (e == 0) {  // first block of the pair: d at bytes 0-1, codes 2 bytes in
+                    dbits = raw[h][0] & 0xffffu;
 #pragma unroll
-                for (int g = 0; g < 4; ++g) code[g] = __builtin_amdgcn_alignbyte(dw[q0 + g + 1], dw[q0 + g], 2);
-            } else {  // block starts 2 bytes into a dword: codes aligned
-                const int q0 = (18 * j - 2) / 4;
-                dbits = dw[q0] >> 16;
+                    for (int g = 0; g < 4; ++g) code[g] = __builtin_amdgcn_alignbyte(raw[h][g + 1], raw[h][g], 2);
+                } else {  // second: d at bytes 18-19, codes at 20 .. 35 (aligned)
+                    dbits = raw[h][4] >> 16;
 #pragma unroll
-                for (int g = 0; g < 4; ++g) code[g] = dw[q0 + 1 + g];
-            }
-            uint32_t* dst = bq + blk * kBlockStride + 2 * fr;
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const uint64_t v = q4_codes_to_s8(code[g]);
-                *reinterpret_cast<uint2*>(dst + g * kGroupStride) =
-                    make_uint2(static_cast<uint32_t>(v), static_cast<uint32_t>(v >> 32));
-            }
-            bs[blk * TN + fr] = half_bits_to_float(dbits) * 0.0625f;
-        }
-    };
-
-    struct AFrag {
-        uint64_t e[MW], o[MW];      // codes of blocks b, b + 1
-        float xe[MW][4], xo[MW][4];  // their scales, rows 4 lg .. 4 lg + 3
-    };
-    auto load_a = [&](int64_t b, AFrag& A) {
-#pragma unroll
-        for (int mi = 0; mi < MW; ++mi) {
-            const int64_t mt = tm * (MW * WM) + wm * MW + mi;
-            const uint4 v = *reinterpret_cast<const uint4*>(xa + ((mt * (nb >> 1) + (b >> 1)) * kWave + lane) * 16);
-            A.e[mi] = static_cast<uint64_t>(v.x) | (static_cast<uint64_t>(v.y) << 32);
-            A.o[mi] = static_cast<uint64_t>(v.z) | (static_cast<uint64_t>(v.w) << 32);
-            const float4 de = *reinterpret_cast<const float4*>(xd + (mt * nb + b) * 16 + 4 * lg);
-            const float4 dq = *reinterpret_cast<const float4*>(xd + (mt * nb + b + 1) * 16 + 4 * lg);
-            A.xe[mi][0] = de.x; A.xe[mi][1] = de.y; A.xe[mi][2] = de.z; A.xe[mi][3] = de.w;
-            A.xo[mi][0] = dq.x; A.xo[mi][1] = dq.y; A.xo[mi][2] = dq.z; A.xo[mi][3] = dq.w;
-        }
-    };
-
-    float acc[MW][NW][4];
-#pragma unroll
-    for (int mi = 0; mi < MW; ++mi)
-#pragma unroll
-        for (int ni = 0; ni < NW; ++ni)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) acc[mi][ni][r] = 0.0f;
-
-    // block pair jp of the chunk in LDS (blocks b, b + 1 of the row), activations from A
-    auto mul_pair = [&](int jp, const AFrag& A, int64_t b) {
-        const int je = 2 * jp, jo = 2 * jp + 1;
-#pragma unroll
-        for (int ni = 0; ni < NW; ++ni) {
-            const int r = (wn * NW + ni) * 16 + li;
-            const uint2 be2 = *reinterpret_cast<const uint2*>(bq + je * kBlockStride + lg * kGroupStride + 2 * r);
-            const uint2 bo2 = *reinterpret_cast<const uint2*>(bq + jo * kBlockStride + lg * kGroupStride + 2 * r);
-            const float se = bs[je * TN + r];
-            const float so = bs[jo * TN + r];
-            const uint64_t be = static_cast<uint64_t>(be2.x) | (static_cast<uint64_t>(be2.y) << 32);
-            const uint64_t bo = static_cast<uint64_t>(bo2.x) | (static_cast<uint64_t>(bo2.y) << 32);
-#pragma unroll
-            for (int mi = 0; mi < MW; ++mi) {
-                const v4i zero = {0, 0, 0, 0};
-                const v4i De = __builtin_amdgcn_mfma_i32_16x16x32_i8(static_cast<long>(A.e[mi]), static_cast<long>(be),
-                                                                      zero, 0, 0, 0);
-                const v4i Do = __builtin_amdgcn_mfma_i32_16x16x32_i8(static_cast<long>(A.o[mi]), static_cast<long>(bo),
-                                                                      zero, 0, 0, 0);
-                if constexpr (MODE == kModeISum) {
-                    const int n = n0 + r;
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        const int64_t m = (tm * (MW * WM) + wm * MW + mi) * 16 + 4 * lg + q;
-                        if (m < M && n >= isn0 && n < isn1) {
-                            int32_t* dst = isum + (m * (isn1 - isn0) + (n - isn0)) * nb + b;
-                            dst[0] = De[q] >> 4;
-                            dst[1] = Do[q] >> 4;
-                        }
-                    }
-                } else {
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        acc[mi][ni][q] = fmaf(static_cast<float>(De[q]), se * A.xe[mi][q], acc[mi][ni][q]);
-                        acc[mi][ni][q] = fmaf(static_cast<float>(Do[q]), so * A.xo[mi][q], acc[mi][ni][q]);
-                    }
+                    for (int g = 0; g < 4; ++g) code[g] = raw[h][5 + g];
                 }
+                uint32_t lo[4], hi[4];
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    lo[g] = ((code[g] << 4) ^ 0x88888880u) & 0xF0F0F0F0u;  // elements 4g .. 4g + 3
+                    hi[g] = (code[g] ^ 0x88888888u) & 0xF0F0F0F0u;         // elements 16 + 4g .. 16 + 4g + 3
+                }
+                bq[j * kQStride + row] = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+                bq[j * kQStride + TN + row] = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+                // d_w / 16 = H + L exactly (11 significant bits)
+                const float d16 = half_bits_to_float(dbits) * 0.0625f;
+                const uint32_t H = __float_as_uint(d16) & 0xffff0000u;
+                const uint32_t L = __float_as_uint(d16 - __uint_as_float(H)) & 0xffff0000u;
+                bsc[j * kSStride + row] = make_uint2((H >> 16) | H, (H >> 16) | L);
+                bsc[j * kSStride + TN + row] = make_uint2((L >> 16) | L, 0u);
             }
         }
     };
 
-    AFrag A0, A1;
-    load_a(0, A0);
+    // activation operands of block b (tile-major layout: 1 KB of codes and
+    // 512 B of scale terms per 32-row tile and block)
+    const int64_t at = tm * 2 + wm;  // 32-row tile
+    const uint4* arow = reinterpret_cast<const uint4*>(xq) + at * nb * kWave + lane;
+    const uint4* srow = xs + at * nb * 32 + li;
+    struct AOp {
+        v4i q;
+        uint2 s;
+    };
+    auto load_a = [&](int64_t b, AOp& A) {
+        A.q = __builtin_bit_cast(v4i, arow[b * kWave]);
+        const uint2* sp = reinterpret_cast<const uint2*>(srow + b * 32);
+        A.s = sp[lg];
+    };
+
+    float acc[2][16];
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[t][r] = 0.0f;
+
+    auto mul_block = [&](int j, const AOp& A, int64_t b) {
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            const v4i bw = __builtin_bit_cast(v4i, bq[j * kQStride + lg * TN + 32 * t + li]);
+            const v16i zi = {};
+            const v16i D = __builtin_amdgcn_mfma_i32_32x32x32_i8(A.q, bw, zi, 0, 0, 0);
+            if constexpr (MODE == kModeISum) {
+                const int n = n0 + 32 * t + li;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int64_t m = tm * TM + 32 * wm + 8 * (r / 4) + 4 * lg + (r % 4);
+                    if (m < M && n >= isn0 && n < isn1) isum[(m * (isn1 - isn0) + (n - isn0)) * nb + b] = D[r] >> 4;
+                }
+            } else {
+                const uint2 ws = bsc[j * kSStride + lg * TN + 32 * t + li];
+                const v16f zf = {};
+                const v16f S = __builtin_amdgcn_mfma_f32_32x32x8bf16_1k(__builtin_bit_cast(s4, A.s),
+                                                                        __builtin_bit_cast(s4, ws), zf, 0, 0, 0);
+#pragma unroll
+                for (int r = 0; r < 16; ++r) acc[t][r] = fmaf(static_cast<float>(D[r]), S[r], acc[t][r]);
+            }
+        }
+    };
+
+    // This wave's blocks are b = wk, wk + 2, ... (nb is even).  Their
+    // activation operands stream through a ring of four register sets,
+    // three blocks ahead of the multiplies and across chunk boundaries; the
+    // loads are unconditional (past the wave's last block they read it
+    // again).  A chunk gives every wave 8 blocks (4 in a last half chunk),
+    // so the ring is back at slot 0 at every chunk start.
+    const int64_t blast = nb - 2 + wk;
+    auto ahead = [&](int64_t b) { return b < blast ? b : blast; };
+    AOp A0, A1, A2, A3;
+    load_a(ahead(wk), A0);
+    load_a(ahead(wk + 2), A1);
+    load_a(ahead(wk + 4), A2);
     fetch(0);
     for (int c0 = 0; c0 < nb; c0 += KC) {
         __syncthreads();  // every wave is done with the previous chunk
         stash();
         __syncthreads();
         if (c0 + KC < nb) fetch(c0 + KC);
-        const int npair = min(KC, nb - c0) >> 1;  // 4 or 8: even
-        for (int jp = 0; jp < npair; jp += 2) {
-            load_a(c0 + 2 * jp + 2, A1);
-            mul_pair(jp, A0, c0 + 2 * jp);
-            const int64_t nxt = c0 + 2 * jp + 4;
-            load_a(nxt < nb ? nxt : nb - 2, A0);
-            mul_pair(jp + 1, A1, c0 + 2 * jp + 2);
+        const int nblk = min(KC, nb - c0);  // 16, or 8 for a last half chunk
+        for (int j = wk; j < nblk; j += 8) {
+            const int64_t b = c0 + j;
+            load_a(ahead(b + 6), A3);
+            mul_block(j, A0, b);
+            load_a(ahead(b + 8), A0);
+            mul_block(j + 2, A1, b + 2);
+            load_a(ahead(b + 10), A1);
+            mul_block(j + 4, A2, b + 4);
+            load_a(ahead(b + 12), A2);
+            mul_block(j + 6, A3, b + 6);
         }
     }
     if constexpr (MODE == kModeY) {
+        __syncthreads();  // the LDS planes are free
+        float* red = reinterpret_cast<float*>(bq);
+        if (wk == 1) {
 #pragma unroll
-        for (int mi = 0; mi < MW; ++mi)
+            for (int t = 0; t < 2; ++t)
 #pragma unroll
-            for (int ni = 0; ni < NW; ++ni) {
-                const int n = n0 + (wn * NW + ni) * 16 + li;
+                for (int r = 0; r < 16; ++r) red[((wm * 2 + t) * 16 + r) * kWave + lane] = acc[t][r];
+        }
+        __syncthreads();
+        if (wk == 0) {
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const int64_t m = (tm * (MW * WM) + wm * MW + mi) * 16 + 4 * lg + q;
-                    if (m < M && n < N) out[m * N + n] = acc[mi][ni][q];
+            for (int t = 0; t < 2; ++t) {
+                const int n = n0 + 32 * t + li;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const float v = acc[t][r] + red[((wm * 2 + t) * 16 + r) * kWave + lane];
+                    const int64_t m = tm * TM + 32 * wm + 8 * (r / 4) + 4 * lg + (r % 4);
+                    if (m < M && n < N) out[m * N + n] = v;
                 }
             }
+        }
     }
 }
 
@@ -982,9 +1086,8 @@ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 // qmm_dot_kernel.
 constexpr int64_t kDotMaxG = 200;
 
-// The two MFMA tilings: wide (64 x 64 per workgroup, 32 x 32 per wave) and
+// The two MFMA tilings: wide (64 x 64 per workgroup, qmm_wide_kernel) and
 // narrow (16 x 16 per workgroup, the four waves splitting K).
-#define QMM_WIDE 2, 2, 2, 2, 1, 32
 #define QMM_NARROW 1, 1, 1, 1, 4, 128
 constexpr int kWideTM = 64, kWideTN = 64, kNarrowTM = 16, kNarrowTN = 16;
 
@@ -1033,24 +1136,36 @@ QmmPlan plan_qmm(int64_t N, int64_t K, int64_t M) {
         p.xrows = p.tiles_m * kNarrowTM;
     }
     p.q_bytes = align256(static_cast<size_t>(p.xrows) * static_cast<size_t>(K));
-    p.d_bytes = align256(static_cast<size_t>(p.xrows) * static_cast<size_t>(nb) * sizeof(float));
+    // scales: float32, or the wide tiling's 16-byte bf16 operand pairs
+    const size_t dsize = p.path == kPathWide ? sizeof(uint4) : sizeof(float);
+    p.d_bytes = align256(static_cast<size_t>(p.xrows) * static_cast<size_t>(nb) * dsize);
     p.p_bytes = p.ks > 1 ? align256(static_cast<size_t>(p.ks) * static_cast<size_t>(M) * static_cast<size_t>(N) *
                                     sizeof(float))
                          : 0;
     return p;
 }
 
-template <bool FRAG>
+template <int LAYOUT>
 hipError_t launch_quantize(const float* x, int8_t* q, float* d, int64_t K, int64_t M, int64_t Mrows,
                            hipStream_t stream) {
-    const int64_t groups = Mrows * (K / 32);
-    int64_t blocks = ceil_div(groups * 8, kBlockThreads);
-    const int64_t cap = static_cast<int64_t>(device_cus()) * 64;
-    if (blocks > cap) blocks = cap;
-    const bool vec_x = (reinterpret_cast<uintptr_t>(x) & 15) == 0;
-    const bool vec_q = (reinterpret_cast<uintptr_t>(q) & 3) == 0;
-    hipLaunchKernelGGL((quantize_q8_kernel<FRAG>), dim3(static_cast<unsigned>(blocks)), dim3(kBlockThreads), 0,
-                       stream, x, q, d, K, M, Mrows, vec_x, vec_q);
+    if constexpr (LAYOUT == kLayoutSplit) {
+        const int64_t items = (Mrows / 32) * (K / 32);
+        int64_t blocks = ceil_div(items, kWavesPerBlock);
+        const int64_t cap = static_cast<int64_t>(device_cus()) * 16;
+        if (blocks > cap) blocks = cap;
+        const bool vec_x = (reinterpret_cast<uintptr_t>(x) & 15) == 0;
+        hipLaunchKernelGGL(quantize_q8_tiles_kernel, dim3(static_cast<unsigned>(blocks)), dim3(kBlockThreads), 0,
+                           stream, x, q, reinterpret_cast<uint4*>(d), K, M, Mrows, vec_x);
+    } else {
+        const int64_t groups = Mrows * (K / 32);
+        int64_t blocks = ceil_div(groups * 8, kBlockThreads);
+        const int64_t cap = static_cast<int64_t>(device_cus()) * 64;
+        if (blocks > cap) blocks = cap;
+        const bool vec_x = (reinterpret_cast<uintptr_t>(x) & 15) == 0;
+        const bool vec_q = (reinterpret_cast<uintptr_t>(q) & 3) == 0;
+        hipLaunchKernelGGL((quantize_q8_kernel<LAYOUT>), dim3(static_cast<unsigned>(blocks)), dim3(kBlockThreads), 0,
+                           stream, x, q, d, K, M, Mrows, vec_x, vec_q);
+    }
     return hipGetLastError();
 }
 
@@ -1086,8 +1201,9 @@ hipError_t launch_wide(const QmmPlan& p, const void* W, const int8_t* xa, const 
     for (int64_t tm0 = 0; tm0 < p.tiles_m; tm0 += mt_slice) {
         const int64_t tms = (p.tiles_m - tm0 < mt_slice) ? p.tiles_m - tm0 : mt_slice;
         const int64_t nwg = tms * p.tiles_n;
-        hipLaunchKernelGGL((qmm_wide_kernel<16, MODE>), dim3(static_cast<unsigned>(nwg)), dim3(kBlockThreads), 0,
-                           stream, static_cast<const uint8_t*>(W), xa, xd, y, isum, static_cast<int>(N), M,
+        hipLaunchKernelGGL((qmm_wide_kernel<MODE>), dim3(static_cast<unsigned>(nwg)), dim3(kBlockThreads), 0,
+                           stream, static_cast<const uint8_t*>(W), xa, reinterpret_cast<const uint4*>(xd), y, isum,
+                           static_cast<int>(N), M,
                            static_cast<int>(K / 32), tm0, tms, p.tiles_n, nwg, static_cast<int>(isn0),
                            static_cast<int>(isn1));
         const hipError_t e = hipGetLastError();
@@ -1205,7 +1321,7 @@ size_t qmm_ws_bytes(int64_t N, int64_t K, int64_t M) {
 }
 
 hipError_t launch_quantize_q8(const float* x, int8_t* q, float* d, int64_t K, int64_t M, hipStream_t stream) {
-    return launch_quantize<false>(x, q, d, K, M, M, stream);
+    return launch_quantize<kLayoutRows>(x, q, d, K, M, M, stream);
 }
 
 hipError_t launch_qmm_q8act(const void* W, const float* x, float* y, int32_t* isum, int64_t isn0, int64_t isn1,
@@ -1215,8 +1331,9 @@ hipError_t launch_qmm_q8act(const void* W, const float* x, float* y, int32_t* is
     float* d = reinterpret_cast<float*>(static_cast<char*>(ws) + p.q_bytes);
     float* part = reinterpret_cast<float*>(static_cast<char*>(ws) + p.q_bytes + p.d_bytes);
     const bool mfma = p.path == kPathWide || p.path == kPathNarrow;
-    hipError_t e = mfma ? launch_quantize<true>(x, q, d, K, M, p.xrows, stream)
-                        : launch_quantize<false>(x, q, d, K, M, M, stream);
+    hipError_t e = p.path == kPathWide     ? launch_quantize<kLayoutSplit>(x, q, d, K, M, p.xrows, stream)
+                   : p.path == kPathNarrow ? launch_quantize<kLayoutFrag>(x, q, d, K, M, p.xrows, stream)
+                                           : launch_quantize<kLayoutRows>(x, q, d, K, M, M, stream);
     if (e != hipSuccess) return e;
     if (!mfma) return launch_dot(p, W, q, d, isum ? nullptr : y, isum, isn0, isn1, N, K, M, stream);
     if (p.path == kPathWide) {
