@@ -13,8 +13,14 @@ weights from HBM, as a decoder streams each layer's weights once per token.
 Metric: effective GB/s = algorithmic bytes (weights + activations + outputs)
 per step / time per step, and the fraction of the 8 TB/s HBM peak.
 
-Usage: python bench.py [--gpus 1] [--steps 200] [--warmup 20] [--no-rows] [--no-cpu-baseline]
-Prints one JSON line.
+Timing: the K timed steps are split into --reps windows (3 by default) with
+events between them; `value` and `ms_per_step` are the median window, and
+the windows' spread is reported.  Per-kernel durations are the median of
+--reps repetitions of a back-to-back loop of each entry point alone.
+
+Usage: python bench.py [--gpus 1] [--steps 300] [--warmup 20] [--reps 3] [--no-rows] [--no-cpu-baseline]
+Prints one JSON line.  `--trace-summary DIR` / `--pmc-summary DIR` instead
+print the markdown summaries kept under profiles/ from rocprofv3 CSV output.
 """
 from __future__ import annotations
 
@@ -28,6 +34,7 @@ import time
 import numpy as np
 
 HBM_PEAK_GBS = 8000.0  # MI355X published HBM3E bandwidth
+INT8_MFMA_PEAK_TOPS = 5000.0  # MI355X published dense int8 MFMA rate
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
@@ -53,34 +60,71 @@ def unit_grid(N: int, K: int, cus: int, per_cu: int) -> int:
 def profiled_traffic(kernel: str, grid: int):
     """HBM bytes (read + write) per launch of `kernel` from the counter
     summary, or None when it is missing or was taken on other sources."""
-    import hashlib
     path = os.path.join(ROOT, TRAFFIC_PROFILE)
     try:
         text = open(path).read()
     except OSError:
         return None
-    for src, digest in re.findall(r"source_sha256 (\S+) ([0-9a-f]{64})", text):
-        try:
-            with open(os.path.join(ROOT, src), "rb") as f:
-                if hashlib.sha256(f.read()).hexdigest() != digest:
-                    return None
-        except OSError:
-            return None
+    if not _sources_match(text):
+        return None
     for name, g, rd, wr in re.findall(r"<!-- traffic (.+?) grid=(\d+) read=(\d+) write=(\d+) -->", text):
         if name == kernel and int(g) == grid:
             return int(rd) + int(wr)
     return None
 
 
+TRACE_PROFILE = os.path.join("profiles", "qmv_bench_workloads_kernel_trace.md")
+
+
+def _sources_match(text):
+    """True when every `source_sha256 <file> <digest>` line of a profile
+    summary matches the file as it is now."""
+    import hashlib
+    pairs = re.findall(r"source_sha256 (\S+) ([0-9a-f]{64})", text)
+    if not pairs:
+        return False
+    for src, digest in pairs:
+        try:
+            with open(os.path.join(ROOT, src), "rb") as f:
+                if hashlib.sha256(f.read()).hexdigest() != digest:
+                    return False
+        except OSError:
+            return False
+    return True
+
+
+def profiled_trace_us(kernel: str, grid: int):
+    """Mean kernel-trace duration (us) of `kernel` at `grid` workgroups from the
+    committed trace summary, or None when it is missing or was taken on other
+    sources."""
+    try:
+        text = open(os.path.join(ROOT, TRACE_PROFILE)).read()
+    except OSError:
+        return None
+    if not _sources_match(text):
+        return None
+    for name, g, mean in re.findall(r"<!-- trace (.+?) grid=(\d+) mean_us=([0-9.]+) -->", text):
+        if name == kernel and int(g) == grid:
+            return float(mean)
+    return None
+
+
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--steps", type=int, default=300)
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--slots", type=int, default=4)
     p.add_argument("--no-rows", action="store_true", help="skip the per-row measurements of the other workloads")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
+    p.add_argument("--reps", type=int, default=3,
+                   help="timing windows inside the K timed steps (and repetitions of each per-launch loop); "
+                        "the reported rates are their medians")
+    p.add_argument("--trace-summary", metavar="DIR", help="only print the markdown summary of a rocprofv3 "
+                   "--kernel-trace --output-format csv run written to DIR, and exit")
+    p.add_argument("--pmc-summary", metavar="DIR", help="only print the markdown summary of rocprofv3 --pmc "
+                   "--output-format csv runs written under DIR, and exit")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MB",
                    help="only run 10 device-to-device copies of MB megabytes (a plain copy kernel of known "
                         "size, used to scale the HBM traffic counters) and exit")
@@ -101,6 +145,11 @@ def copy_calibration(mb: int) -> None:
 
 def main():
     args = parse()
+    if args.trace_summary or args.pmc_summary:
+        cmd = os.environ.get("PROFILE_COMMAND", "(command not recorded)")
+        sys.stdout.write(trace_summary(args.trace_summary, cmd) if args.trace_summary
+                         else pmc_summary(args.pmc_summary, cmd))
+        return
     if args.copy_calibration:
         copy_calibration(args.copy_calibration)
         return
@@ -137,47 +186,66 @@ def main():
 
     # per-kernel durations first: each entry point alone, back to back over
     # the slot sets, between one pair of events on the stream the kernels run
-    # on (events between every launch would add their own queue packets).
-    # They also bring the GPU to its sustained-load clocks before the steps
-    # are timed.
-    def per_launch(fn):
+    # on (events between every launch would add their own queue packets),
+    # repeated --reps times; the median repetition is reported.  They also
+    # bring the GPU to its sustained-load clocks before the steps are timed.
+    stream = torch.cuda.current_stream()
+
+    def per_launch(fn, iters):
         for i in range(5):
             fn(i)
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        a.record()
-        for i in range(args.steps):
-            fn(i)
-        b.record()
-        torch.cuda.synchronize()
-        return a.elapsed_time(b) / args.steps
+        reps = []
+        for _ in range(args.reps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            a.record(stream)
+            for i in range(iters):
+                fn(i)
+            b.record(stream)
+            torch.cuda.synchronize()
+            reps.append(a.elapsed_time(b) / iters)
+        return reps
 
-    t_single = per_launch(lambda i: qmv.qmv_q4_0(slots[i % S][0], xd, y1, N, K, 1))
-    t_pair = per_launch(lambda i: qmv.qmv_q4_0_geglu(slots[i % S][1], slots[i % S][2], xd, h, N, K, 1))
+    iters = max(args.steps // max(args.reps, 1), 1)
+    t_single = per_launch(lambda i: qmv.qmv_q4_0(slots[i % S][0], xd, y1, N, K, 1), iters)
+    t_pair = per_launch(lambda i: qmv.qmv_q4_0_geglu(slots[i % S][1], slots[i % S][2], xd, h, N, K, 1), iters)
 
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
 
-    # whole-step timing
-    E0, E1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # whole-step timing: exactly K steps between two synchronizations, split
+    # into --reps windows by events on the kernels' stream
+    nw = max(1, min(args.reps, args.steps))
+    bounds = [args.steps * w // nw for w in range(nw + 1)]
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(nw + 1)]
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
-    E0.record()
-    for i in range(args.steps):
-        step(i)
-    E1.record()
+    ev[0].record(stream)
+    for w in range(nw):
+        for i in range(bounds[w], bounds[w + 1]):
+            step(i)
+        ev[w + 1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
-    ms_step = E0.elapsed_time(E1) / args.steps
+    windows = [ev[w].elapsed_time(ev[w + 1]) / (bounds[w + 1] - bounds[w]) for w in range(nw)]
+    ms_step = _median(windows)
+    ms_total = ev[0].elapsed_time(ev[nw]) / args.steps
 
     value = bytes_step / (ms_step * 1e-3) / 1e9
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
     kernels = {}
-    for entry, b, tk in (("qmv_q4_0", bytes_single, t_single), ("qmv_q4_0_geglu", bytes_pair, t_pair)):
+    for entry, b, reps in (("qmv_q4_0", bytes_single, t_single), ("qmv_q4_0_geglu", bytes_pair, t_pair)):
         sym, per_cu = KERNEL_OF[entry]
-        grid = unit_grid(N, K, torch.cuda.get_device_properties(dev).multi_processor_count, per_cu)
+        grid = unit_grid(N, K, cus, per_cu)
+        tk = _median(reps)
+        trace = profiled_trace_us(sym, grid)
         kernels[entry] = {"kernel": sym, "workgroups": grid, "bytes": b, "us": round(tk * 1e3, 3),
-                          "GB/s": round(b / (tk * 1e-3) / 1e9, 1), "hbm_traffic_bytes": profiled_traffic(sym, grid)}
+                          "us_reps": [round(r * 1e3, 3) for r in reps], "spread": round(_spread(reps), 4),
+                          "GB/s": round(b / (tk * 1e-3) / 1e9, 1), "frac_of_hbm_peak": round(b / (tk * 1e-3) / 1e9 /
+                                                                                          HBM_PEAK_GBS, 4),
+                          "trace_us": trace, "us_over_trace": round(tk * 1e3 / trace, 4) if trace else None,
+                          "hbm_traffic_bytes": profiled_traffic(sym, grid)}
     dom_entry, dom = max(kernels.items(), key=lambda kv: kv[1]["us"])
     roofline = {
         "bound": "hbm",
@@ -188,6 +256,12 @@ def main():
         "frac": round(dom["GB/s"] / HBM_PEAK_GBS, 4),
         "traffic": dom["hbm_traffic_bytes"],
         "traffic_source": TRAFFIC_PROFILE if dom["hbm_traffic_bytes"] is not None else None,
+        "duration_source": f"median of {args.reps} back-to-back loops of {iters} launches, HIP events on the "
+                           "launch stream",
+        "trace_us": dom["trace_us"],
+        "trace_source": TRACE_PROFILE if dom["trace_us"] is not None else None,
+        "frac_from_trace": round(dom["bytes"] / (dom["trace_us"] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)
+        if dom["trace_us"] else None,
     }
 
     ceiling = read_ceiling(torch, qmv, dev, {"single": wbytes, "pair": 2 * wbytes})
@@ -209,6 +283,9 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_step, 5),
+        "ms_per_step_windows": [round(w, 5) for w in windows],
+        "window_spread": round(_spread(windows), 4),
+        "ms_per_step_all_steps": round(ms_total, 5),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -231,6 +308,17 @@ def main():
     print(json.dumps(out))
 
 
+def _median(v):
+    v = sorted(v)
+    n = len(v)
+    return v[n // 2] if n % 2 else 0.5 * (v[n // 2 - 1] + v[n // 2])
+
+
+def _spread(v):
+    """(max - min) / median of a list of timings."""
+    return (max(v) - min(v)) / _median(v) if v else 0.0
+
+
 def read_ceiling(torch, qmv, dev, sizes, iters=50):
     """The plain streaming-read rate (qmvdbg_stream_read: every byte loaded once
     with coalesced 16-byte loads) at the byte counts of the timed launches,
@@ -243,7 +331,7 @@ def read_ceiling(torch, qmv, dev, sizes, iters=50):
         copies = max(2 if nbytes >= 500_000_000 else 4, -(-1_000_000_000 // nbytes))
         bufs = [torch.full((nbytes,), i + 1, dtype=torch.uint8, device=dev) for i in range(copies)]
         best = None
-        for wg in (2048, 4096, 8192, 16384):
+        for wg in (256, 512, 768, 1024, 2048, 4096):
             ms = _time_loop(torch, lambda i: qmv.qmvdbg_stream_read(bufs[i % copies], nbytes, word, wg), iters)
             if best is None or ms < best[0]:
                 best = (ms, wg)
@@ -253,17 +341,23 @@ def read_ceiling(torch, qmv, dev, sizes, iters=50):
     return out
 
 
-def _time_loop(torch, fn, iters, warm=5):
+def _time_loop(torch, fn, iters, warm=5, reps=3):
+    """Median over `reps` repetitions of the mean time (ms) of `iters`
+    back-to-back calls, events on the current stream."""
     for i in range(warm):
         fn(i)
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for i in range(iters):
-        fn(i)
-    e1.record()
-    torch.cuda.synchronize()
-    return e0.elapsed_time(e1) / iters  # ms
+    out = []
+    stream = torch.cuda.current_stream()
+    for _ in range(reps):
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(iters):
+            fn(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        out.append(e0.elapsed_time(e1) / iters)
+    return _median(out)
 
 
 def measure_rows(torch, qmv, synth, dev):
@@ -453,9 +547,13 @@ def measure_rows(torch, qmv, synth, dev):
     res["copy_256MB_read_plus_write"] = {"us": ms * 1e3, "bytes": 2 * a.numel(), "GB/s": 2 * a.numel() / ms / 1e6}
     del a, bb
     for v in res.values():
+        if "GB/s" in v:
+            v["frac_of_hbm_peak"] = v["GB/s"] / HBM_PEAK_GBS
+        if "int_TOPS" in v:
+            v["frac_of_int8_mfma_peak"] = v["int_TOPS"] / INT8_MFMA_PEAK_TOPS
         for key in list(v):
             if isinstance(v[key], float):
-                v[key] = round(v[key], 2)
+                v[key] = round(v[key], 4 if key.startswith("frac") else 2)
     return res
 
 
@@ -491,6 +589,112 @@ def cpu_baseline(synth, Ws, Wg, Wu, x, N, K, bytes_step, seconds):
         "c1_4096x4096_single_thread_s": round(t1, 4),
         "cpu_model": _cpu_model(),
     }
+
+
+# ------------------------------------------------------------ profile summaries
+# Sources whose sha256 is recorded in a summary: the numbers in it are valid
+# while these are unchanged.
+PROFILED_SOURCES = ("quantized_dequant_matrix_amd/csrc/gemv.hip", "quantized_dequant_matrix_amd/csrc/qmm.hip",
+                    "quantized_dequant_matrix_amd/csrc/topk.hip", "quantized_dequant_matrix_amd/csrc/stream.hip",
+                    "quantized_dequant_matrix_amd/csrc/qmv_device.h", "quantized_dequant_matrix_amd/build.py")
+
+
+def _kernel_symbol(name: str) -> str:
+    """'void qmv::(anonymous namespace)::k<1, 2>(args)' -> 'qmv::k<1, 2>'."""
+    name = name.replace("(anonymous namespace)::", "")
+    if name.startswith("void "):
+        name = name[5:]
+    depth = 0
+    for i, ch in enumerate(name):
+        if ch == "<":
+            depth += 1
+        elif ch == ">":
+            depth -= 1
+        elif ch == "(" and depth == 0:
+            return name[:i]
+    return name
+
+
+def _csv_rows(directory: str, suffix: str):
+    import csv
+    import glob
+    rows = []
+    for path in sorted(glob.glob(os.path.join(directory, "**", "*" + suffix), recursive=True)):
+        with open(path, newline="") as f:
+            rows.extend(csv.DictReader(f))
+    return rows
+
+
+def _workgroups(r) -> int:
+    grid = int(r.get("Grid_Size") or r.get("Grid_Size_X") or 0)
+    wg = int(r.get("Workgroup_Size") or r.get("Workgroup_Size_X") or 1)
+    return grid // max(wg, 1)
+
+
+def _source_lines():
+    import hashlib
+    out = ["Sources the numbers were taken on (sha256):", ""]
+    for src in PROFILED_SOURCES:
+        with open(os.path.join(ROOT, src), "rb") as f:
+            out.append(f"- source_sha256 {src} {hashlib.sha256(f.read()).hexdigest()}")
+    return out
+
+
+def trace_summary(directory: str, command: str) -> str:
+    """Markdown table of a rocprofv3 --kernel-trace run: per kernel and grid,
+    calls and mean / median / min / max durations, plus a machine-readable
+    line per kernel that profiled_trace_us() reads."""
+    import statistics
+    groups = {}
+    for r in _csv_rows(directory, "kernel_trace.csv"):
+        key = (_kernel_symbol(r["Kernel_Name"]), _workgroups(r))
+        groups.setdefault(key, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1000.0)
+    lines = ["# Kernel trace of bench.py: every kernel the benchmark launches", "",
+             "Command (from the repository root, one MI355X):", "", "```", command, "```", "",
+             "Durations from the kernel trace, per kernel symbol and grid (workgroups):", "",
+             "| kernel | grid | calls | mean us | median us | min us | max us |", "|---|---|---|---|---|---|---|"]
+    marks = []
+    for (k, g), v in sorted(groups.items(), key=lambda kv: -sum(kv[1])):
+        lines.append(f"| `{k}` | {g} | {len(v)} | {statistics.mean(v):.2f} | {statistics.median(v):.2f} | "
+                     f"{min(v):.2f} | {max(v):.2f} |")
+        marks.append(f"<!-- trace {k} grid={g} mean_us={statistics.mean(v):.3f} -->")
+    return "\n".join(lines + [""] + _source_lines() + [""] + marks) + "\n"
+
+
+def pmc_summary(directory: str, command: str) -> str:
+    """Markdown table of rocprofv3 --pmc runs (every run_counter_collection.csv
+    under `directory`): per kernel and grid, the median of each counter over
+    its dispatches.  FETCH_SIZE and WRITE_SIZE (KiB per dispatch) are scaled
+    by what they read for the plain copies of bench.py --copy-calibration
+    (bytes per copy known), and written as machine-readable traffic lines."""
+    import statistics
+    vals = {}
+    for r in _csv_rows(directory, "counter_collection.csv"):
+        key = (_kernel_symbol(r["Kernel_Name"]), _workgroups(r))
+        vals.setdefault(key, {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    med = {k: {c: statistics.median(v) for c, v in cs.items()} for k, cs in vals.items()}
+    counters = sorted({c for cs in med.values() for c in cs})
+    # calibration: the copy kernel that moves 256 MB per dispatch
+    cal = {}
+    for (k, g), cs in med.items():
+        if "copy" in k.lower() or "Copy" in k:
+            for c in ("FETCH_SIZE", "WRITE_SIZE"):
+                if c in cs and cs[c] > 0:
+                    cal[c] = 256e6 / (cs[c] * 1024.0)
+    lines = ["# Counters of bench.py's kernels (rocprofv3 --pmc)", "", "Commands (from the repository root, one "
+             "MI355X):", "", "```", command, "```", "", "Medians over each kernel's dispatches:", "",
+             "| kernel | grid | " + " | ".join(counters) + " |", "|---|---|" + "---|" * len(counters)]
+    marks = []
+    for (k, g), cs in sorted(med.items(), key=lambda kv: -kv[1].get("FETCH_SIZE", kv[1].get("SQ_WAVES", 0))):
+        lines.append(f"| `{k}` | {g} | " + " | ".join(f"{cs[c]:.6g}" if c in cs else "" for c in counters) + " |")
+        if "FETCH_SIZE" in cs and "WRITE_SIZE" in cs and cal.get("FETCH_SIZE") and cal.get("WRITE_SIZE"):
+            rd = cs["FETCH_SIZE"] * 1024.0 * cal["FETCH_SIZE"]
+            wr = cs["WRITE_SIZE"] * 1024.0 * cal["WRITE_SIZE"]
+            marks.append(f"<!-- traffic {k} grid={g} read={rd:.0f} write={wr:.0f} -->")
+    if cal:
+        lines += ["", "Copy calibration (bytes per KiB counted): " +
+                  ", ".join(f"{c} x{cal[c] * 1024.0:.1f}" for c in sorted(cal))]
+    return "\n".join(lines + [""] + _source_lines() + [""] + marks) + "\n"
 
 
 def _cpu_model():

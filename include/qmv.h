@@ -296,7 +296,8 @@ int qmvdbg_sample_f32(const float* top_val, const int32_t* top_idx, const float*
 
 /* A plain streaming read, the measured ceiling for the kernels above: reads
  * the `bytes` bytes at p (a multiple of 16, p 16-byte aligned) once with
- * coalesced 16-byte loads, on a grid of `workgroups` 256-thread workgroups.
+ * coalesced 16-byte loads (each wave a contiguous 4 KB chunk per round), on
+ * a grid of `workgroups` 256-thread workgroups.
  * out[w], w < workgroups, receives the XOR of the 32-bit words that
  * workgroup w read (0 if none), so the XOR of out[0 .. workgroups) is the
  * XOR of the whole buffer.  out must hold `workgroups` words.
