@@ -39,9 +39,10 @@
  *   do not share output or workspace buffers.
  * Errors.  All arguments are checked on the host before anything is
  *   enqueued; on any error nothing is launched and the call returns the
- *   status below [captable section 9: legal dimensions are checked at
- *   dispatch, not assumed; a path may not silently drop work; captable
- *   findings F6, F13 and F17 are the defects this rules out]:
+ *   status below [captable section 9: dimensions are validated when a
+ *   call is made rather than taken for granted, and no path may skip part
+ *   of the work without an error; captable findings F6, F13 and F17 are the
+ *   defects this rules out]:
  *     QMV_ERR_NULL       a required pointer is NULL
  *     QMV_ERR_SHAPE      N, M < 1; M > 65535; K < 32 or K % 32 != 0 (K % 256
  *                        != 0 for Q4_K, Q6_K); a size or a byte count overflows int64, or
@@ -78,8 +79,9 @@ typedef enum {
 const char* qmv_status_str(int status);
 
 /* y[m][n] = sum_k w[n][k] * x[m][k], Q4_0 weights.
- * [roadmap K2 step 1: direct Q4_0 matrix-vector with fused dequantization
- *  and F32 accumulation; captable section 1: q4_f32_matvec, Q4_0 x f32]
+ * [roadmap K2 step 1: the Q4_0 matrix-vector product that decodes blocks
+ *  inside the dot product and sums in float32; captable section 1:
+ *  q4_f32_matvec, Q4_0 weights times float32 activations]
  * M > 1 is M independent matrix-vector products. */
 int qmv_q4_0(const void* W, const float* x, float* y,
              int64_t N, int64_t K, int64_t M, hipStream_t stream);
@@ -111,9 +113,9 @@ int qmv_q6_k(const void* W, const float* x, float* y,
  *            (e = 255 is NaN and makes the row's output NaN);
  *   w = E2M1(code) * 2^(e - 127).  K % 32 == 0; both planes 16-byte
  *   aligned.  The codes are converted with gfx950's packed FP4 conversion.
- * [captable section 1: mxfp4_matvec, MXFP4 16 B / 32 + external e8m0
- *  scales x f32; roadmap K5: a weight layout whose decode maps to native
- *  packed operations] */
+ * [captable section 1: mxfp4_matvec, 16 code bytes per 32 weights with the
+ *  E8M0 scales held outside the blocks; roadmap K5: the next weight layout
+ *  should decode with the hardware's packed conversions] */
 int qmv_mxfp4(const void* W_codes, const void* W_scales, const float* x, float* y,
               int64_t N, int64_t K, int64_t M, hipStream_t stream);
 
@@ -121,7 +123,7 @@ int qmv_mxfp4(const void* W_codes, const void* W_scales, const float* x, float* 
  * u = W_up x[m], both Q4_0 [N][K], gelu the tanh form
  * v/2 (1 + tanh(sqrt(2/pi) (v + 0.044715 v^3))).  Both matrices are read
  * in one launch.
- * [roadmap K1: GELU-gated FFN; K2 step 5: gated GELU FFN projection pair;
+ * [roadmap K1: GELU-gated FFN; K2 step 5: the FFN's gate and up projections;
  *  captable section 4: q4k_ffn_gate_up (two matrices, one dispatch) and
  *  geglu_gelu_tanh] */
 int qmv_q4_0_geglu(const void* W_gate, const void* W_up, const float* x, float* h,
@@ -151,7 +153,7 @@ int qmv_q6_k_geglu_down(const void* W_down, const float* g, const float* u, floa
  * outputs float32 [M][Nq], [M][Nk], [M][Nv].  K % 256 == 0.  Each output
  * row is the same product qmv_q4_k / qmv_q6_k form for that row.
  * Rows longer than 16128 weights take one launch per matrix.
- * [captable section 2: q4k_q6k_qkv_proj, Q4_K Q/K + Q6_K V x f32 in one
+ * [captable section 2: q4k_q6k_qkv_proj, Q and K in Q4_K with V in Q6_K in one
  *  dispatch, and the route that selects it for the (Q4_K, Q4_K, Q6_K) mix;
  *  finding F2: a QKV route must honour V's own format] */
 int qmv_q4_k_q6_k_qkv(const void* Wq, const void* Wk, const void* Wv, const float* x,

@@ -171,9 +171,9 @@ static void dequant_q6_k_block(const uint8_t* b, double* w) {
 }
 
 /* ------------------------------------------------------------------ */
-/* MXFP4 [captable section 1: mxfp4_matvec, "MXFP4 16B/32 + ext e8m0   */
-/* scales"; roadmap K5: a weight layout whose decode maps to native     */
-/* packed operations].  Two planes per matrix:                          */
+/* MXFP4 [captable section 1: mxfp4_matvec, 16 code bytes per 32     */
+/* weights, E8M0 scales outside the blocks; roadmap K5: a next weight   */
+/* layout that decodes with packed hardware conversions].  Two planes: */
 /*   codes  [N][K/32][16 B]: 32 four-bit E2M1 elements per block,       */
 /*   scales [N][K/32] bytes: one E8M0 exponent per block.               */
 /* Reading (the pages give the sizes and the word "ext" only):          */
@@ -285,8 +285,8 @@ int oracle_dequant_row(int fmt, const uint8_t* row, int64_t K, double* w) {
 /*   S[m][i] = sum_k |w[r_i][k] * x[m][k]|    (scale of the tolerance)  */
 /* for the selected rows r_i (rows == NULL: all N rows in order).      */
 /* Output layout: [M][nrows].                                          */
-/* [roadmap K1: matrix-vector; roadmap K2 step 1: direct Q4_0          */
-/* matrix-vector with fused dequantization and F32 accumulation]       */
+/* [roadmap K1: matrix-vector; roadmap K2 step 1: the Q4_0 product    */
+/* that decodes blocks inside the dot product, float32 sums]           */
 /* Pinned by exact rational brute force (K = 32, 64), e_i columns and  */
 /* linearity in tests/test_oracle_qmv.py.                              */
 /* ------------------------------------------------------------------ */
@@ -347,7 +347,7 @@ double oracle_gelu_tanh(double v) {
     return 0.5 * v * (1.0 + tanh(inner));
 }
 
-/* Gated pair: h = gelu(g) * u   [roadmap K2 step 5: gated GELU FFN projection pair] */
+/* Gated pair: h = gelu(g) * u   [roadmap K2 step 5: the FFN's gate and up projections] */
 void oracle_geglu(const double* g, const double* u, int64_t n, double* h) {
     for (int64_t i = 0; i < n; ++i) h[i] = oracle_gelu_tanh(g[i]) * u[i];
 }

@@ -3,9 +3,10 @@
 // GELU pair.
 //
 // What is computed: y[n] = sum_k w[n][k] x[k] with w decoded from the block
-// formats on the fly ["Gemma 4 M4 Max kernel roadmap", K2 step 1: direct
-// Q4_0 matrix-vector with fused dequantization and F32 accumulation; step 5:
-// gated GELU FFN projection pair; "Metal kernel capability table", section 1
+// formats on the fly ["Gemma 4 M4 Max kernel roadmap", K2 step 1: a Q4_0
+// matrix-vector product whose dot product decodes the blocks itself and sums
+// in float32; step 5: the FFN's gate and up projections; "Metal kernel
+// capability table", section 1
 // (q4_f32_matvec, q4k_matvec, q6k_matvec) and section 4 (q4k_ffn_gate_up:
 // both matrices in one dispatch)].
 //

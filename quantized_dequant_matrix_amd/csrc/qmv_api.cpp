@@ -1,9 +1,10 @@
 // C ABI of libqmv.so: argument checking and dispatch.  Every check runs on
 // the host before anything is enqueued; on any error nothing is launched.
 // The checks follow the dispatcher contract the "Metal kernel capability
-// table" (section 9) asks for: legal dimensions are checked at dispatch, a
-// path may not silently drop work, silent truncation is a defect (findings
-// F6, F13, F17 there).
+// table" (section 9) asks for: every dimension is validated when the call
+// is made rather than taken for granted, no path drops part of the work
+// unannounced, and cutting an input short without an error counts as a bug
+// (findings F6, F13, F17 there).
 #include "../../include/qmv.h"
 
 #include <hip/hip_runtime_api.h>
