@@ -615,11 +615,16 @@ def _kernel_symbol(name: str) -> str:
     return name
 
 
-def _csv_rows(directory: str, suffix: str):
+def _csv_rows(directory: str, suffix: str, calibration=None):
+    """Rows of every rocprofv3 CSV named *suffix under directory; with
+    calibration True / False only those of runs written with -o cal /
+    the others."""
     import csv
     import glob
     rows = []
     for path in sorted(glob.glob(os.path.join(directory, "**", "*" + suffix), recursive=True)):
+        if calibration is not None and os.path.basename(path).startswith("cal") != calibration:
+            continue
         with open(path, newline="") as f:
             rows.extend(csv.DictReader(f))
     return rows
@@ -668,16 +673,20 @@ def pmc_summary(directory: str, command: str) -> str:
     by what they read for the plain copies of bench.py --copy-calibration
     (bytes per copy known), and written as machine-readable traffic lines."""
     import statistics
-    vals = {}
-    for r in _csv_rows(directory, "counter_collection.csv"):
-        key = (_kernel_symbol(r["Kernel_Name"]), _workgroups(r))
-        vals.setdefault(key, {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
-    med = {k: {c: statistics.median(v) for c, v in cs.items()} for k, cs in vals.items()}
+    def medians(rows):
+        vals = {}
+        for r in rows:
+            key = (_kernel_symbol(r["Kernel_Name"]), _workgroups(r))
+            vals.setdefault(key, {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+        return {k: {c: statistics.median(v) for c, v in cs.items()} for k, cs in vals.items()}
+
+    med = medians(_csv_rows(directory, "counter_collection.csv", calibration=False))
     counters = sorted({c for cs in med.values() for c in cs})
-    # calibration: the copy kernel that moves 256 MB per dispatch
+    # calibration runs (-o cal): bench.py --copy-calibration 256, ten device
+    # copies of 256 MB (256e6 bytes read and written per dispatch)
     cal = {}
-    for (k, g), cs in med.items():
-        if "copy" in k.lower() or "Copy" in k:
+    for (k, g), cs in medians(_csv_rows(directory, "counter_collection.csv", calibration=True)).items():
+        if "copy" in k.lower():
             for c in ("FETCH_SIZE", "WRITE_SIZE"):
                 if c in cs and cs[c] > 0:
                     cal[c] = 256e6 / (cs[c] * 1024.0)
