@@ -41,7 +41,7 @@ sys.path.insert(0, ROOT)
 # HBM traffic per launch comes from the committed rocprofv3 counter summary
 # (FETCH_SIZE / WRITE_SIZE, scaled by a plain copy); it is reported only while
 # the sources it was measured on are unchanged.
-TRAFFIC_PROFILE = os.path.join("profiles", "qmv_bench_workloads_hbm_traffic.md")
+TRAFFIC_PROFILE = os.path.join("profiles", "qmv_bench_workloads_counters.md")
 # kernel symbol of each timed launch, and its workgroups per CU at most
 KERNEL_OF = {
     "qmv_q4_0": ("qmv::gemv_unit_kernel<0, 1, false, false>", 3),
