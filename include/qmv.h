@@ -175,8 +175,10 @@ int qmv_q4_k_q6_k_qkv(const void* Wq, const void* Wk, const void* Wv, const floa
  * ws: device buffer of at least qmm_q4_0_q8act_ws_bytes(N, K, M) bytes,
  * 16-byte aligned, contents overwritten.  It holds the int8 codes and
  * scales of x (rows padded to the kernel's tile height) and, when the
- * contraction splits K across workgroups (small M), the float32 partial
- * sums.  The size depends on (N, K, M) only; 0 means an invalid shape. */
+ * contraction splits K across workgroups (small M, or the last tiles of a
+ * large grid shared out in K chunks so that every CU gets the same work),
+ * the float32 partial sums.  The size depends on (N, K, M) only; 0 means an
+ * invalid shape. */
 size_t qmm_q4_0_q8act_ws_bytes(int64_t N, int64_t K, int64_t M);
 int qmm_q4_0_q8act(const void* W, const float* x, float* y,
                    int64_t N, int64_t K, int64_t M,

@@ -612,11 +612,35 @@ typedef int v16i __attribute__((ext_vector_type(16)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef short s4 __attribute__((ext_vector_type(4)));
 
+// Which tiles and which chunks of 16 blocks each workgroup of a wide launch
+// takes.  Items 0 .. whole - 1 are whole 64 x 64 tiles; items whole ..
+// whole + parts - 1 share the remaining tiles' chunks, item j taking the
+// units [j units / parts, (j + 1) units / parts) of the unit sequence (tile
+// whole + u / nch, chunk u % nch), at most two tiles each, and write their
+// sums to partial slots that qmm_wide_fixup_kernel adds in chunk order.  A
+// CU holds workgroups i, i + 256 and i + 512 (three resident per CU), so with
+// whole = 2 * 256 every CU gets two whole tiles and one share of the rest:
+// even work instead of three tiles on some CUs and two on others.  Within
+// each kind, consecutive items are dealt to the 8 XCDs so that each XCD gets
+// a contiguous run (the same weight rows for all m-tiles).
+struct WideSchedule {
+    int64_t tm0;      // first m-tile of the launch
+    int64_t tiles_m;  // m-tiles in the launch
+    int tiles_n;
+    int nch;          // chunks of 16 blocks per tile
+    int whole;        // whole-tile items
+    int parts;        // chunk-share items (0: none)
+    int64_t units;    // (tiles - whole) * nch
+};
+
+__host__ __device__ inline int64_t xcd_run(int64_t i, int64_t n) { return n % 8 == 0 ? (i % 8) * (n / 8) + i / 8 : i; }
+__host__ __device__ inline int64_t share_start(int64_t j, const WideSchedule& S) { return j * S.units / S.parts; }
+
 template <int MODE>
 __global__ __launch_bounds__(kBlockThreads)
 void qmm_wide_kernel(const uint8_t* __restrict__ W, const int8_t* __restrict__ xq, const uint4* __restrict__ xs,
-                     float* __restrict__ out, int32_t* __restrict__ isum, int N, int64_t M, int nb, int64_t tm0,
-                     int64_t tiles_m, int tiles_n, int64_t nwg, int isn0, int isn1) {
+                     float* __restrict__ out, float* __restrict__ part, int32_t* __restrict__ isum, int N, int64_t M,
+                     int nb, WideSchedule S, int isn0, int isn1) {
     static_assert(MODE == kModeY || MODE == kModeISum, "y or block sums");
     constexpr int TM = 64, TN = 64, KC = 16;
     // LDS planes, [block j][half g] each TN rows of 16 (or 8) bytes.  The
@@ -629,177 +653,257 @@ void qmm_wide_kernel(const uint8_t* __restrict__ W, const int8_t* __restrict__ x
     __shared__ __align__(16) uint4 bq[KC * kQStride];   // decoded codes, 32.3 KB
     __shared__ __align__(16) uint2 bsc[KC * kSStride];  // scale operands, 16.1 KB
 
-    // Each XCD gets a contiguous run of tiles (same weight rows, all m-tiles).
-    int64_t lin = blockIdx.x;
-    if (nwg % 8 == 0) lin = (lin % 8) * (nwg / 8) + lin / 8;
-    const int64_t tm = tm0 + lin % tiles_m;
-    const int tn = static_cast<int>(lin / tiles_m);
-    const int n0 = tn * TN;
     const int64_t row_bytes = static_cast<int64_t>(nb) * 18;
-
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int lane = threadIdx.x & (kWave - 1);
     const int wm = w & 1;      // activation rows 32 wm .. 32 wm + 31 of the tile
     const int wk = w >> 1;     // blocks wk, wk + 2, ... of each chunk
     const int li = lane & 31;  // A row / B column of the lane
     const int lg = lane >> 5;  // k half of the lane
-
-    // Weight chunk (64 rows x 16 blocks): thread t fetches block pair
-    // fp = t % 8 (36 bytes, 4-byte aligned) of rows fr = t / 8 and fr + 32,
-    // so that eight consecutive lanes read a row's 288 bytes.  A last chunk
-    // of 8 blocks reads (unused) pairs 0 .. 3 again; rows past N read row
-    // N - 1.
     const int fp = threadIdx.x & 7;
     const int fr = threadIdx.x >> 3;
-    const uint8_t* frow0 = W + static_cast<int64_t>(min(n0 + fr, N - 1)) * row_bytes;
-    const uint8_t* frow1 = W + static_cast<int64_t>(min(n0 + fr + 32, N - 1)) * row_bytes;
-    uint32_t raw[2][9];
-    auto fetch = [&](int c0) {
-        const int b0 = c0 + 2 * fp;
-        const int64_t off = static_cast<int64_t>(b0 < nb ? b0 : c0) * 18;
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const uint8_t* src = (h ? frow1 : frow0) + off;
-            const u32x4_a4 a = *reinterpret_cast<const u32x4_a4*>(src);
-            const u32x4_a4 b = *reinterpret_cast<const u32x4_a4*>(src + 16);
-            raw[h][0] = a.x; raw[h][1] = a.y; raw[h][2] = a.z; raw[h][3] = a.w;
-            raw[h][4] = b.x; raw[h][5] = b.y; raw[h][6] = b.z; raw[h][7] = b.w;
-            raw[h][8] = *reinterpret_cast<const uint32_t*>(src + 32);
-        }
-    };
-    auto stash = [&]() {
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const int row = fr + 32 * h;
-#pragma unroll
-            for (int e = 0; e < 2; ++e) {
-                const int j = 2 * fp + e;
-                uint32_t dbits, code[4];
-                if (e == 0) {  // first block of the pair: d at bytes 0-1, codes 2 bytes in
-                    dbits = raw[h][0] & 0xffffu;
-#pragma unroll
-                    for (int g = 0; g < 4; ++g) code[g] = __builtin_amdgcn_alignbyte(raw[h][g + 1], raw[h][g], 2);
-                } else {  // second: d at bytes 18-19, codes at 20 .. 35 (aligned)
-                    dbits = raw[h][4] >> 16;
-#pragma unroll
-                    for (int g = 0; g < 4; ++g) code[g] = raw[h][5 + g];
-                }
-                uint32_t lo[4], hi[4];
-#pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    lo[g] = ((code[g] << 4) ^ 0x88888880u) & 0xF0F0F0F0u;  // elements 4g .. 4g + 3
-                    hi[g] = (code[g] ^ 0x88888888u) & 0xF0F0F0F0u;         // elements 16 + 4g .. 16 + 4g + 3
-                }
-                bq[j * kQStride + row] = make_uint4(lo[0], lo[1], lo[2], lo[3]);
-                bq[j * kQStride + TN + row] = make_uint4(hi[0], hi[1], hi[2], hi[3]);
-                // d_w / 16 = H + L exactly (11 significant bits)
-                const float d16 = half_bits_to_float(dbits) * 0.0625f;
-                const uint32_t H = __float_as_uint(d16) & 0xffff0000u;
-                const uint32_t L = __float_as_uint(d16 - __uint_as_float(H)) & 0xffff0000u;
-                bsc[j * kSStride + row] = make_uint2((H >> 16) | H, (H >> 16) | L);
-                bsc[j * kSStride + TN + row] = make_uint2((L >> 16) | L, 0u);
-            }
-        }
-    };
 
-    // activation operands of block b (tile-major layout: 1 KB of codes and
-    // 512 B of scale terms per 32-row tile and block)
-    const int64_t at = tm * 2 + wm;  // 32-row tile
-    const uint4* arow = reinterpret_cast<const uint4*>(xq) + at * nb * kWave + lane;
-    const uint4* srow = xs + at * nb * 32 + li;
-    struct AOp {
-        v4i q;
-        uint2 s;
-    };
-    auto load_a = [&](int64_t b, AOp& A) {
-        A.q = __builtin_bit_cast(v4i, arow[b * kWave]);
-        const uint2* sp = reinterpret_cast<const uint2*>(srow + b * 32);
-        A.s = sp[lg];
-    };
-
-    float acc[2][16];
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[t][r] = 0.0f;
-
-    auto mul_block = [&](int j, const AOp& A, int64_t b) {
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-            const v4i bw = __builtin_bit_cast(v4i, bq[j * kQStride + lg * TN + 32 * t + li]);
-            const v16i zi = {};
-            const v16i D = __builtin_amdgcn_mfma_i32_32x32x32_i8(A.q, bw, zi, 0, 0, 0);
-            if constexpr (MODE == kModeISum) {
-                const int n = n0 + 32 * t + li;
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int64_t m = tm * TM + 32 * wm + 8 * (r / 4) + 4 * lg + (r % 4);
-                    if (m < M && n >= isn0 && n < isn1) isum[(m * (isn1 - isn0) + (n - isn0)) * nb + b] = D[r] >> 4;
-                }
-            } else {
-                const uint2 ws = bsc[j * kSStride + lg * TN + 32 * t + li];
-                const v16f zf = {};
-                const v16f S = __builtin_amdgcn_mfma_f32_32x32x8bf16_1k(__builtin_bit_cast(s4, A.s),
-                                                                        __builtin_bit_cast(s4, ws), zf, 0, 0, 0);
-#pragma unroll
-                for (int r = 0; r < 16; ++r) acc[t][r] = fmaf(static_cast<float>(D[r]), S[r], acc[t][r]);
-            }
-        }
-    };
-
-    // This wave's blocks are b = wk, wk + 2, ... (nb is even).  Their
-    // activation operands stream through a ring of four register sets,
-    // three blocks ahead of the multiplies and across chunk boundaries; the
-    // loads are unconditional (past the wave's last block they read it
-    // again).  A chunk gives every wave 8 blocks (4 in a last half chunk),
-    // so the ring is back at slot 0 at every chunk start.
-    const int64_t blast = nb - 2 + wk;
-    auto ahead = [&](int64_t b) { return b < blast ? b : blast; };
-    AOp A0, A1, A2, A3;
-    load_a(ahead(wk), A0);
-    load_a(ahead(wk + 2), A1);
-    load_a(ahead(wk + 4), A2);
-    fetch(0);
-    for (int c0 = 0; c0 < nb; c0 += KC) {
-        __syncthreads();  // every wave is done with the previous chunk
-        stash();
-        __syncthreads();
-        if (c0 + KC < nb) fetch(c0 + KC);
-        const int nblk = min(KC, nb - c0);  // 16, or 8 for a last half chunk
-        for (int j = wk; j < nblk; j += 8) {
-            const int64_t b = c0 + j;
-            load_a(ahead(b + 6), A3);
-            mul_block(j, A0, b);
-            load_a(ahead(b + 8), A0);
-            mul_block(j + 2, A1, b + 2);
-            load_a(ahead(b + 10), A1);
-            mul_block(j + 4, A2, b + 4);
-            load_a(ahead(b + 12), A2);
-            mul_block(j + 6, A3, b + 6);
+    // this workgroup's segments: (tile, first chunk, end chunk, partial slot)
+    const int64_t item = blockIdx.x;
+    int64_t seg_tile[2];
+    int seg_cb[2], seg_ce[2], nseg;
+    int64_t share = -1;
+    if (item < S.whole) {
+        seg_tile[0] = xcd_run(item, S.whole);
+        seg_cb[0] = 0;
+        seg_ce[0] = S.nch;
+        nseg = 1;
+    } else {
+        share = xcd_run(item - S.whole, S.parts);
+        const int64_t u0 = share_start(share, S), u1 = share_start(share + 1, S);
+        nseg = 0;
+        for (int64_t u = u0; u < u1;) {
+            const int64_t r = u / S.nch;  // remaining tile
+            const int64_t ue = ((r + 1) * S.nch < u1) ? (r + 1) * S.nch : u1;
+            seg_tile[nseg] = S.whole + r;
+            seg_cb[nseg] = static_cast<int>(u - r * S.nch);
+            seg_ce[nseg] = static_cast<int>(ue - r * S.nch);
+            ++nseg;
+            u = ue;
         }
     }
-    if constexpr (MODE == kModeY) {
-        __syncthreads();  // the LDS planes are free
-        float* red = reinterpret_cast<float*>(bq);
-        if (wk == 1) {
+
+    // (unrolled: as a loop the two passes held 60 more VGPRs live)
 #pragma unroll
-            for (int t = 0; t < 2; ++t)
+    for (int sg = 0; sg < 2; ++sg) {
+        if (sg >= nseg) break;
+        const int64_t tile = seg_tile[sg];
+        const int64_t tm = S.tm0 + tile % S.tiles_m;
+        const int n0 = static_cast<int>(tile / S.tiles_m) * TN;
+        const int kb0 = seg_cb[sg] * KC;
+        const int kb1 = min(nb, seg_ce[sg] * KC);
+
+        // Weight chunk (64 rows x 16 blocks): thread t fetches block pair
+        // fp = t % 8 (36 bytes, 4-byte aligned) of rows fr = t / 8 and
+        // fr + 32, so that eight consecutive lanes read a row's 288 bytes.  A
+        // last chunk of 8 blocks reads (unused) pairs 0 .. 3 again; rows past
+        // N read row N - 1.
+        const uint8_t* frow0 = W + static_cast<int64_t>(min(n0 + fr, N - 1)) * row_bytes;
+        const uint8_t* frow1 = W + static_cast<int64_t>(min(n0 + fr + 32, N - 1)) * row_bytes;
+        uint32_t raw[2][9];
+        auto fetch = [&](int c0) {
+            const int b0 = c0 + 2 * fp;
+            const int64_t off = static_cast<int64_t>(b0 < kb1 ? b0 : c0) * 18;
 #pragma unroll
-                for (int r = 0; r < 16; ++r) red[((wm * 2 + t) * 16 + r) * kWave + lane] = acc[t][r];
-        }
-        __syncthreads();
-        if (wk == 0) {
+            for (int h = 0; h < 2; ++h) {
+                const uint8_t* src = (h ? frow1 : frow0) + off;
+                const u32x4_a4 a = *reinterpret_cast<const u32x4_a4*>(src);
+                const u32x4_a4 b = *reinterpret_cast<const u32x4_a4*>(src + 16);
+                raw[h][0] = a.x; raw[h][1] = a.y; raw[h][2] = a.z; raw[h][3] = a.w;
+                raw[h][4] = b.x; raw[h][5] = b.y; raw[h][6] = b.z; raw[h][7] = b.w;
+                raw[h][8] = *reinterpret_cast<const uint32_t*>(src + 32);
+            }
+        };
+        auto stash = [&]() {
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int row = fr + 32 * h;
+#pragma unroll
+                for (int e = 0; e < 2; ++e) {
+                    const int j = 2 * fp + e;
+                    uint32_t dbits, code[4];
+                    if (e == 0) {  // first block of the pair: d at bytes 0-1, codes 2 bytes in
+                        dbits = raw[h][0] & 0xffffu;
+#pragma unroll
+                        for (int g = 0; g < 4; ++g) code[g] = __builtin_amdgcn_alignbyte(raw[h][g + 1], raw[h][g], 2);
+                    } else {  // second: d at bytes 18-19, codes at 20 .. 35 (aligned)
+                        dbits = raw[h][4] >> 16;
+#pragma unroll
+                        for (int g = 0; g < 4; ++g) code[g] = raw[h][5 + g];
+                    }
+                    uint32_t lo[4], hi[4];
+#pragma unroll
+                    for (int g = 0; g < 4; ++g) {
+                        lo[g] = ((code[g] << 4) ^ 0x88888880u) & 0xF0F0F0F0u;  // elements 4g .. 4g + 3
+                        hi[g] = (code[g] ^ 0x88888888u) & 0xF0F0F0F0u;         // elements 16 + 4g .. 16 + 4g + 3
+                    }
+                    bq[j * kQStride + row] = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+                    bq[j * kQStride + TN + row] = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+                    // d_w / 16 = H + L exactly (11 significant bits)
+                    const float d16 = half_bits_to_float(dbits) * 0.0625f;
+                    const uint32_t H = __float_as_uint(d16) & 0xffff0000u;
+                    const uint32_t L = __float_as_uint(d16 - __uint_as_float(H)) & 0xffff0000u;
+                    bsc[j * kSStride + row] = make_uint2((H >> 16) | H, (H >> 16) | L);
+                    bsc[j * kSStride + TN + row] = make_uint2((L >> 16) | L, 0u);
+                }
+            }
+        };
+
+        // activation operands of block b (tile-major layout: 1 KB of codes and
+        // 512 B of scale terms per 32-row tile and block)
+        const int64_t at = tm * 2 + wm;  // 32-row tile
+        const uint4* arow = reinterpret_cast<const uint4*>(xq) + at * nb * kWave + lane;
+        const uint4* srow = xs + at * nb * 32 + li;
+        struct AOp {
+            v4i q;
+            uint2 s;
+        };
+        auto load_a = [&](int64_t b, AOp& A) {
+            A.q = __builtin_bit_cast(v4i, arow[b * kWave]);
+            const uint2* sp = reinterpret_cast<const uint2*>(srow + b * 32);
+            A.s = sp[lg];
+        };
+
+        float acc[2][16];
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[t][r] = 0.0f;
+
+        auto mul_block = [&](int j, const AOp& A, int64_t b) {
 #pragma unroll
             for (int t = 0; t < 2; ++t) {
-                const int n = n0 + 32 * t + li;
+                const v4i bw = __builtin_bit_cast(v4i, bq[j * kQStride + lg * TN + 32 * t + li]);
+                const v16i zi = {};
+                const v16i D = __builtin_amdgcn_mfma_i32_32x32x32_i8(A.q, bw, zi, 0, 0, 0);
+                if constexpr (MODE == kModeISum) {
+                    const int n = n0 + 32 * t + li;
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const float v = acc[t][r] + red[((wm * 2 + t) * 16 + r) * kWave + lane];
-                    const int64_t m = tm * TM + 32 * wm + 8 * (r / 4) + 4 * lg + (r % 4);
-                    if (m < M && n < N) out[m * N + n] = v;
+                    for (int r = 0; r < 16; ++r) {
+                        const int64_t m = tm * TM + 32 * wm + 8 * (r / 4) + 4 * lg + (r % 4);
+                        if (m < M && n >= isn0 && n < isn1)
+                            isum[(m * (isn1 - isn0) + (n - isn0)) * nb + b] = D[r] >> 4;
+                    }
+                } else {
+                    const uint2 ws = bsc[j * kSStride + lg * TN + 32 * t + li];
+                    const v16f zf = {};
+                    const v16f Sc = __builtin_amdgcn_mfma_f32_32x32x8bf16_1k(__builtin_bit_cast(s4, A.s),
+                                                                             __builtin_bit_cast(s4, ws), zf, 0, 0, 0);
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) acc[t][r] = fmaf(static_cast<float>(D[r]), Sc[r], acc[t][r]);
+                }
+            }
+        };
+
+        // This wave's blocks of the segment are b = kb0 + wk, + 2, ... (the
+        // segment has an even block count).  Their activation operands stream
+        // through a ring of four register sets, three blocks ahead of the
+        // multiplies and across chunk boundaries; the loads are unconditional
+        // (past the wave's last block they read it again).  A chunk gives
+        // every wave 8 blocks (4 in a last half chunk), so the ring is back at
+        // slot 0 at every chunk start.
+        const int64_t blast = kb1 - 2 + wk;
+        auto ahead = [&](int64_t b) { return b < blast ? b : blast; };
+        AOp A0, A1, A2, A3;
+        load_a(ahead(kb0 + wk), A0);
+        load_a(ahead(kb0 + wk + 2), A1);
+        load_a(ahead(kb0 + wk + 4), A2);
+        fetch(kb0);
+        for (int c0 = kb0; c0 < kb1; c0 += KC) {
+            __syncthreads();  // every wave is done with the previous chunk (or segment)
+            stash();
+            __syncthreads();
+            if (c0 + KC < kb1) fetch(c0 + KC);
+            const int nblk = min(KC, kb1 - c0);  // 16, or 8 for a last half chunk
+            for (int j = wk; j < nblk; j += 8) {
+                const int64_t b = c0 + j;
+                load_a(ahead(b + 6), A3);
+                mul_block(j, A0, b);
+                load_a(ahead(b + 8), A0);
+                mul_block(j + 2, A1, b + 2);
+                load_a(ahead(b + 10), A1);
+                mul_block(j + 4, A2, b + 4);
+                load_a(ahead(b + 12), A2);
+                mul_block(j + 6, A3, b + 6);
+            }
+        }
+        if constexpr (MODE == kModeY) {
+            __syncthreads();  // the LDS planes are free
+            float* red = reinterpret_cast<float*>(bq);
+            if (wk == 1) {
+#pragma unroll
+                for (int t = 0; t < 2; ++t)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) red[((wm * 2 + t) * 16 + r) * kWave + lane] = acc[t][r];
+            }
+            __syncthreads();
+            if (wk == 0) {
+                // a whole tile goes to y; a share of a tile to its partial
+                // slot [share][segment][64 rows][64 columns]
+                float* slot = share >= 0 ? part + (share * 2 + sg) * (TM * TN) : nullptr;
+#pragma unroll
+                for (int t = 0; t < 2; ++t) {
+                    const int nl = 32 * t + li;
+                    const int n = n0 + nl;
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const float v = acc[t][r] + red[((wm * 2 + t) * 16 + r) * kWave + lane];
+                        const int ml = 32 * wm + 8 * (r / 4) + 4 * lg + (r % 4);
+                        const int64_t m = tm * TM + ml;
+                        if (slot) {
+                            slot[ml * TN + nl] = v;
+                        } else if (m < M && n < N) {
+                            out[m * N + n] = v;
+                        }
+                    }
                 }
             }
         }
+    }
+}
+
+// y of the tiles that the chunk-share items split: the partial sums of each
+// tile added in chunk order (so in share order).  Four workgroups per tile,
+// one float4 of the tile per thread and share; the share bookkeeping is per
+// workgroup.
+__global__ __launch_bounds__(kBlockThreads)
+void qmm_wide_fixup_kernel(const float* __restrict__ part, float* __restrict__ y, int N, int64_t M, WideSchedule S) {
+    constexpr int TM = 64, TN = 64, kParts = TM * TN / 4 / kBlockThreads;
+    static_assert(kParts == 4, "four workgroups per tile");
+    const int64_t r = blockIdx.x / kParts;  // remaining tile
+    const int quarter = blockIdx.x % kParts;
+    const int64_t tile = S.whole + r;
+    const int64_t tm = S.tm0 + tile % S.tiles_m;
+    const int n0 = static_cast<int>(tile / S.tiles_m) * TN;
+    const int64_t u0 = r * S.nch, u1 = (r + 1) * S.nch;
+    // shares j0 .. j1 hold the tile's units u0 .. u1 - 1, in chunk order: the
+    // share holding unit u is the last j with j units / parts <= u, that is
+    // ((u + 1) parts - 1) / units; only j0 may have begun on the tile before
+    const int64_t j0 = ((u0 + 1) * S.parts - 1) / S.units;
+    const int64_t j1 = (u1 * S.parts - 1) / S.units;
+    const int f4 = quarter * kBlockThreads + static_cast<int>(threadIdx.x);  // float4 of the tile
+    const int first_seg = share_start(j0, S) < u0 ? 1 : 0;
+    float4 v = reinterpret_cast<const float4*>(part + (j0 * 2 + first_seg) * (TM * TN))[f4];
+    for (int64_t q = j0 + 1; q <= j1; ++q) {
+        const float4 p = reinterpret_cast<const float4*>(part + q * 2 * (TM * TN))[f4];
+        v.x += p.x;
+        v.y += p.y;
+        v.z += p.z;
+        v.w += p.w;
+    }
+    const int e = 4 * f4;
+    const int64_t m = tm * TM + e / TN;
+    const int n = n0 + e % TN;
+    const float o[4] = {v.x, v.y, v.z, v.w};
+    if (m < M) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+            if (n + c < N) y[m * N + n + c] = o[c];
     }
 }
 
@@ -1101,8 +1205,31 @@ struct QmmPlan {
     int64_t tiles_m = 0;
     int tiles_n = 0, ks = 1, kb = 0;
     int64_t xrows = 0;  // activation rows in the workspace (padded to the tile height)
+    int whole = 0, parts = 0;  // the wide tiling's item split (wide_schedule)
     size_t q_bytes = 0, d_bytes = 0, p_bytes = 0;
 };
+
+// The wide tiling's workgroups are resident three per CU (48.4 KB of LDS
+// each), and a CU receives workgroups i, i + C and i + 2C of a grid of at
+// most 3C.  With C < T < 3C tiles and T % C != 0, a grid of one workgroup
+// per tile leaves some CUs a tile more than others; instead the last
+// T - floor(T / C) C tiles are cut into C equal shares of chunks.  The split
+// is planned for C = 256 (the MI355X count) so that workspace sizes do not
+// depend on the device; a device with another count runs one workgroup per
+// tile.
+constexpr int kWideCUs = 256;
+
+void wide_schedule(int64_t tiles, int64_t nch, int* whole, int* parts) {
+    const int64_t per = tiles / kWideCUs;
+    // (the shares are never empty: at least one chunk each)
+    if (tiles > kWideCUs && tiles < 3 * kWideCUs && (tiles % kWideCUs) * nch >= kWideCUs) {
+        *whole = static_cast<int>(per * kWideCUs);
+        *parts = kWideCUs;
+    } else {
+        *whole = static_cast<int>(tiles);
+        *parts = 0;
+    }
+}
 
 QmmPlan plan_qmm(int64_t N, int64_t K, int64_t M) {
     QmmPlan p;
@@ -1118,6 +1245,7 @@ QmmPlan plan_qmm(int64_t N, int64_t K, int64_t M) {
         p.ks = 1;
         p.kb = static_cast<int>(nb);
         p.xrows = p.tiles_m * kWideTM;
+        if (p.tiles_m * p.tiles_n < (int64_t{1} << 30)) wide_schedule(p.tiles_m * p.tiles_n, ceil_div(nb, 16), &p.whole, &p.parts);
     } else {
         p.path = kPathNarrow;
         p.tiles_m = ceil_div(M, kNarrowTM);
@@ -1142,6 +1270,8 @@ QmmPlan plan_qmm(int64_t N, int64_t K, int64_t M) {
     p.p_bytes = p.ks > 1 ? align256(static_cast<size_t>(p.ks) * static_cast<size_t>(M) * static_cast<size_t>(N) *
                                     sizeof(float))
                          : 0;
+    // the wide tiling's partial slots: two 64 x 64 float32 tiles per share
+    if (p.parts > 0) p.p_bytes = static_cast<size_t>(p.parts) * 2 * kWideTM * kWideTN * sizeof(float);
     return p;
 }
 
@@ -1191,23 +1321,40 @@ hipError_t launch_mfma(const QmmPlan& p, const void* W, const int8_t* xa, const 
 }
 
 // The wide path: qmm_wide_kernel over all tiles, in slices of m-tiles that
-// keep the grid within 2^30 workgroups.
+// keep the grid within 2^30 workgroups; with a chunk-share split (one slice),
+// qmm_wide_fixup_kernel then writes the split tiles' y.
 template <int MODE>
-hipError_t launch_wide(const QmmPlan& p, const void* W, const int8_t* xa, const float* xd, float* y,
+hipError_t launch_wide(const QmmPlan& p, const void* W, const int8_t* xa, const float* xd, float* y, float* part,
                        int32_t* isum, int64_t isn0, int64_t isn1, int64_t N, int64_t K, int64_t M,
                        hipStream_t stream) {
     int64_t mt_slice = (int64_t{1} << 30) / p.tiles_n;
     mt_slice = mt_slice < p.tiles_m ? mt_slice : p.tiles_m;
+    const int64_t nb = K / 32;
+    const bool split = p.parts > 0 && device_cus() == kWideCUs;
     for (int64_t tm0 = 0; tm0 < p.tiles_m; tm0 += mt_slice) {
         const int64_t tms = (p.tiles_m - tm0 < mt_slice) ? p.tiles_m - tm0 : mt_slice;
-        const int64_t nwg = tms * p.tiles_n;
+        const int64_t tiles = tms * p.tiles_n;
+        WideSchedule S;
+        S.tm0 = tm0;
+        S.tiles_m = tms;
+        S.tiles_n = p.tiles_n;
+        S.nch = static_cast<int>(ceil_div(nb, 16));
+        S.whole = split ? p.whole : static_cast<int>(tiles);
+        S.parts = split ? p.parts : 0;
+        S.units = (tiles - S.whole) * S.nch;
+        const int64_t nwg = static_cast<int64_t>(S.whole) + S.parts;
         hipLaunchKernelGGL((qmm_wide_kernel<MODE>), dim3(static_cast<unsigned>(nwg)), dim3(kBlockThreads), 0,
-                           stream, static_cast<const uint8_t*>(W), xa, reinterpret_cast<const uint4*>(xd), y, isum,
-                           static_cast<int>(N), M,
-                           static_cast<int>(K / 32), tm0, tms, p.tiles_n, nwg, static_cast<int>(isn0),
+                           stream, static_cast<const uint8_t*>(W), xa, reinterpret_cast<const uint4*>(xd), y, part,
+                           isum, static_cast<int>(N), M, static_cast<int>(nb), S, static_cast<int>(isn0),
                            static_cast<int>(isn1));
-        const hipError_t e = hipGetLastError();
+        hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
+        if (MODE == kModeY && S.parts > 0) {
+            hipLaunchKernelGGL(qmm_wide_fixup_kernel, dim3(static_cast<unsigned>(4 * (tiles - S.whole))),
+                               dim3(kBlockThreads), 0, stream, part, y, static_cast<int>(N), M, S);
+            e = hipGetLastError();
+            if (e != hipSuccess) return e;
+        }
     }
     return hipSuccess;
 }
@@ -1337,8 +1484,8 @@ hipError_t launch_qmm_q8act(const void* W, const float* x, float* y, int32_t* is
     if (e != hipSuccess) return e;
     if (!mfma) return launch_dot(p, W, q, d, isum ? nullptr : y, isum, isn0, isn1, N, K, M, stream);
     if (p.path == kPathWide) {
-        return isum ? launch_wide<kModeISum>(p, W, q, d, nullptr, isum, isn0, isn1, N, K, M, stream)
-                    : launch_wide<kModeY>(p, W, q, d, y, nullptr, 0, 0, N, K, M, stream);
+        return isum ? launch_wide<kModeISum>(p, W, q, d, nullptr, part, isum, isn0, isn1, N, K, M, stream)
+                    : launch_wide<kModeY>(p, W, q, d, y, part, nullptr, 0, 0, N, K, M, stream);
     }
     // the narrow tiling: the block-sum mode runs the same grid, K splits included
     if (isum) return launch_mfma<QMM_NARROW, kModeISum>(p, W, q, d, nullptr, isum, isn0, isn1, N, K, M, stream);

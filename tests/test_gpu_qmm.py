@@ -100,10 +100,12 @@ def test_blocksums_bit_exact(M, n0, n1):
     assert np.array_equal(got, ref_blocksums(W, x, N, K, M, n0, n1))
 
 
-@pytest.mark.parametrize("N,K,M", [(4160, 512, 520), (4160, 768, 520), (8200, 256, 512)])
+@pytest.mark.parametrize("N,K,M", [(4160, 512, 520), (4160, 768, 520), (8200, 256, 512), (4600, 768, 520)])
 def test_blocksums_wide_ragged(N, K, M):
     """The wide tiling on every row, with M off the 64-row tiles, N on and off
-    them, and K / 32 = 16, 24 and 8 blocks (whole and half weight chunks)."""
+    them, and K / 32 = 16, 24 and 8 blocks (whole and half weight chunks).
+    (4600, 768, 520) has 648 tiles: 512 whole-tile workgroups and 256 that
+    share the last 136 tiles' 272 chunks, one or two chunks each."""
     assert qmm_path(N, K, M) == "wide"
     say(f"qmvdbg_qmm_q4_0_q8act_blocksums wide N={N} K={K} M={M}")
     W, x = synth.problem("q4_0", N, K, M, 11 * N + K + M)
@@ -181,6 +183,25 @@ def test_qmm_wide_ragged_sampled():
     assert np.all(np.isfinite(y))
 
 
+@pytest.mark.parametrize("N,K,M", [(4600, 768, 520), (4160, 4352, 520)])
+def test_qmm_wide_shared_tiles_sampled(N, K, M):
+    """Grids of 648 and 585 tiles on the wide tiling: 512 workgroups take
+    whole tiles and 256 share the chunks of the rest (272 and 657 chunks of
+    16 blocks, the last of each tile half full for K / 32 = 136), whose
+    partial sums a second kernel adds.  Rows sampled across the whole-tile
+    and the shared part (tile t covers rows 64 (t // 9) .. 64 (t // 9) + 63)."""
+    assert qmm_path(N, K, M) == "wide"
+    say(f"qmm_q4_0_q8act wide tiling, shared tiles N={N} K={K} M={M}, sampled rows")
+    W, x = synth.problem("q4_0", N, K, M, 5 * N + K)
+    y = gpu_qmm(W, x, N, K, M)
+    rng = np.random.default_rng(N + K)
+    rows = np.unique(np.concatenate([[0, 63, 3583, 3584, 3647, 3648, N - 65, N - 64, N - 1],
+                                     rng.choice(N, 40, replace=False)]))
+    yr, S = _qmm_ref(W, x, N, K, M, rows=rows)
+    assert_within(y[:, rows], yr, oracle.float_tol(S), "wide shared tiles")
+    assert np.all(np.isfinite(y))
+
+
 @pytest.mark.parametrize("N,K,M", [(1, 32, 1), (9, 96, 2), (65, 256, 5), (200, 5376, 17), (31, 16640, 3)])
 def test_qmm_shapes(N, K, M):
     say(f"qmm_q4_0_q8act N={N} K={K} M={M}")
@@ -190,12 +211,13 @@ def test_qmm_shapes(N, K, M):
     assert_within(y, yr, oracle.float_tol(S), "qmm")
 
 
-@pytest.mark.parametrize("N,K,M", [(300, 21504, 16), (4096, 2048, 512)])
+@pytest.mark.parametrize("N,K,M", [(300, 21504, 16), (4096, 2048, 512), (4600, 2048, 520)])
 def test_qmm_integer_valued_is_exact(N, K, M):
     """Unit weight scales and one 127 in every activation block (d_x = 1):
     y is the integer sum of the block sums, below 2^24 in every partial sum,
     so it must be exact in any order -- on the narrow (M = 16) and the wide
-    (M = 512) int8 MFMA tilings."""
+    (M = 512) int8 MFMA tilings, and the wide tiling with shared tiles whose
+    partial sums are added by a second kernel (M = 520)."""
     say(f"qmm_q4_0_q8act integer-valued case N={N} K={K} M={M} ({qmm_path(N, K, M)})")
     rng = np.random.default_rng(8 + M)
     q = rng.integers(0, 16, size=(N * K // 32, 32), dtype=np.uint8)
