@@ -134,7 +134,8 @@ def test_blocksums_wide_extreme_codes():
 
 @pytest.mark.parametrize("N,K,M,n0,n1", [(5, 64, 1, 0, 5), (70, 256, 3, 3, 69), (33, 5408, 2, 0, 33),
                                          (129, 4096, 16, 64, 129), (64, 2048, 40, 0, 64), (200, 512, 1, 7, 9),
-                                         (300, 16640, 5, 250, 300)])
+                                         (300, 16640, 5, 250, 300), (300, 3328, 1, 0, 300),
+                                         (129, 10752, 1, 5, 120), (70, 51200, 1, 0, 70)])
 def test_blocksums_shapes(N, K, M, n0, n1):
     say(f"qmvdbg_qmm_q4_0_q8act_blocksums N={N} K={K} M={M} rows {n0}..{n1} ({qmm_path(N, K, M)})")
     W, x = synth.problem("q4_0", N, K, M, N * M + K)
@@ -202,7 +203,8 @@ def test_qmm_wide_shared_tiles_sampled(N, K, M):
     assert np.all(np.isfinite(y))
 
 
-@pytest.mark.parametrize("N,K,M", [(1, 32, 1), (9, 96, 2), (65, 256, 5), (200, 5376, 17), (31, 16640, 3)])
+@pytest.mark.parametrize("N,K,M", [(1, 32, 1), (9, 96, 2), (65, 256, 5), (200, 5376, 17), (31, 16640, 3),
+                                   (300, 3328, 1), (129, 10752, 1), (70, 51200, 1), (3, 256, 1)])
 def test_qmm_shapes(N, K, M):
     say(f"qmm_q4_0_q8act N={N} K={K} M={M}")
     W, x = synth.problem("q4_0", N, K, M, 3 * N + K + M)
@@ -211,13 +213,38 @@ def test_qmm_shapes(N, K, M):
     assert_within(y, yr, oracle.float_tol(S), "qmm")
 
 
-@pytest.mark.parametrize("N,K,M", [(300, 21504, 16), (4096, 2048, 512), (4600, 2048, 520)])
+def test_qmm_m1_unaligned_activations():
+    """M = 1 with the activation row 4 bytes off 16-byte alignment (the
+    quantizer then reads it with scalar loads): the block sums bit for bit and
+    y within tolerance, at K = 21504 (each lane of the dot kernel three
+    256-element units) and K = 512 (one)."""
+    qmv = _qmv()
+    for N, K in [(700, 21504), (90, 512)]:
+        say(f"qmm_q4_0_q8act M=1 N={N} K={K}, x at a 4-byte offset")
+        W, x = synth.problem("q4_0", N, K, 1, 31 * N + K)
+        xd = torch.empty(K + 1, dtype=torch.float32, device="cuda:0")
+        xd[1:] = dev(x.reshape(-1))
+        xv = xd[1:]
+        assert xv.data_ptr() % 16 == 4
+        wsb = qmv.qmm_q4_0_q8act_ws_bytes(N, K, 1)
+        ws = torch.empty(wsb, dtype=torch.uint8, device="cuda:0")
+        y = empty((1, N))
+        qmv.qmm_q4_0_q8act(dev(W), xv, y, N, K, 1, ws, wsb)
+        yr, S = _qmm_ref(W, x, N, K, 1)
+        assert_within(host(y), yr, oracle.float_tol(S), "M=1 unaligned x")
+        isum = empty((1, N, K // 32), dtype=torch.int32)
+        qmv.qmvdbg_qmm_q4_0_q8act_blocksums(dev(W), xv, isum, N, K, 1, 0, N, ws, wsb)
+        assert np.array_equal(host(isum), ref_blocksums(W, x, N, K, 1))
+
+
+@pytest.mark.parametrize("N,K,M", [(300, 21504, 16), (4096, 2048, 512), (4600, 2048, 520), (5376, 21504, 1)])
 def test_qmm_integer_valued_is_exact(N, K, M):
     """Unit weight scales and one 127 in every activation block (d_x = 1):
     y is the integer sum of the block sums, below 2^24 in every partial sum,
     so it must be exact in any order -- on the narrow (M = 16) and the wide
-    (M = 512) int8 MFMA tilings, and the wide tiling with shared tiles whose
-    partial sums are added by a second kernel (M = 520)."""
+    (M = 512) int8 MFMA tilings, the wide tiling with shared tiles whose
+    partial sums are added by a second kernel (M = 520), and the M = 1 dot
+    kernel."""
     say(f"qmm_q4_0_q8act integer-valued case N={N} K={K} M={M} ({qmm_path(N, K, M)})")
     rng = np.random.default_rng(8 + M)
     q = rng.integers(0, 16, size=(N * K // 32, 32), dtype=np.uint8)
