@@ -1191,9 +1191,10 @@ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 constexpr int64_t kDotMaxG = 200;
 
 // The two MFMA tilings: wide (64 x 64 per workgroup, qmm_wide_kernel) and
-// narrow (16 x 16 per workgroup, the four waves splitting K).
-#define QMM_NARROW 1, 1, 1, 1, 4, 128
-constexpr int kWideTM = 64, kWideTN = 64, kNarrowTM = 16, kNarrowTN = 16;
+// narrow (16 x 32 per workgroup: each wave two 16 x 16 tiles sharing one
+// activation load, the four waves splitting K, chunks of 64 blocks).
+#define QMM_NARROW 1, 2, 1, 1, 4, 64
+constexpr int kWideTM = 64, kWideTN = 64, kNarrowTM = 16, kNarrowTN = 32;
 
 enum QmmPath : int { kPathDot = 0, kPathGeneric = 1, kPathWide = 2, kPathNarrow = 3 };
 

@@ -46,7 +46,7 @@ def ref_blocksums(W, x, N, K, M, n0=0, n1=None):
 
 def qmm_path(N, K, M):
     """The tiling qmm_q4_0_q8act picks for (N, K, M) (wide: 64 x 64 tiles,
-    at least 512 of them; narrow: 16 x 16 tiles; else the M = 1 kernels)."""
+    at least 512 of them; narrow: 16 x 32 tiles; else the M = 1 kernels)."""
     if M == 1 or K % 256:
         return "dot"
     return "wide" if -(-M // 64) * -(-N // 64) >= 512 else "narrow"
