@@ -625,16 +625,19 @@ typedef short s4 __attribute__((ext_vector_type(4)));
 // a contiguous run (the same weight rows for all m-tiles).
 struct WideSchedule {
     int64_t tm0;      // first m-tile of the launch
-    int64_t tiles_m;  // m-tiles in the launch
-    int tiles_n;
+    int64_t tiles_m;  // m-tiles in the launch (tile t: m-tile t % tiles_m, n-tile t / tiles_m)
     int nch;          // chunks of 16 blocks per tile
     int whole;        // whole-tile items
     int parts;        // chunk-share items (0: none)
     int64_t units;    // (tiles - whole) * nch
 };
 
-__host__ __device__ inline int64_t xcd_run(int64_t i, int64_t n) { return n % 8 == 0 ? (i % 8) * (n / 8) + i / 8 : i; }
-__host__ __device__ inline int64_t share_start(int64_t j, const WideSchedule& S) { return j * S.units / S.parts; }
+// Item i of n consecutive items of one kind -> its rank in that kind, such
+// that XCD i % 8 (where consecutive workgroups land) gets ranks
+// (i % 8) n / 8 .. (i % 8 + 1) n / 8 - 1.
+__device__ inline int64_t xcd_run(int64_t i, int64_t n) { return n % 8 == 0 ? (i % 8) * (n / 8) + i / 8 : i; }
+// First unit of share j.
+__device__ inline int64_t share_start(int64_t j, const WideSchedule& S) { return j * S.units / S.parts; }
 
 template <int MODE>
 __global__ __launch_bounds__(kBlockThreads)
@@ -1338,7 +1341,6 @@ hipError_t launch_wide(const QmmPlan& p, const void* W, const int8_t* xa, const 
         WideSchedule S;
         S.tm0 = tm0;
         S.tiles_m = tms;
-        S.tiles_n = p.tiles_n;
         S.nch = static_cast<int>(ceil_div(nb, 16));
         S.whole = split ? p.whole : static_cast<int>(tiles);
         S.parts = split ? p.parts : 0;
