@@ -16,7 +16,8 @@ per step / time per step, and the fraction of the 8 TB/s HBM peak.
 Timing: the K timed steps are split into --reps windows (3 by default) with
 events between them; `value` and `ms_per_step` are the median window, and
 the windows' spread is reported.  Per-kernel durations are the median of
---reps repetitions of a back-to-back loop of each entry point alone.
+--reps repetitions of a back-to-back loop of each entry point alone, rotating
+over all twelve matrices of the slot sets (780 MB).
 
 Usage: python bench.py [--gpus 1] [--steps 300] [--warmup 20] [--reps 3] [--no-rows] [--no-cpu-baseline]
 Prints one JSON line.  `--trace-summary DIR` / `--pmc-summary DIR` instead
@@ -206,9 +207,17 @@ def main():
             reps.append(a.elapsed_time(b) / iters)
         return reps
 
+    # The three matrices of every slot set have the same shape, so the
+    # per-launch loops rotate over all 3 S of them (12 x 65 MB at S = 4, three
+    # times the 256 MB last-level cache): the single matrix through each in
+    # turn, the pair through the disjoint pairs (0, 1), (2, 3), ... of them, so
+    # a matrix comes back only after all the others.
+    mats = [m for sl in slots for m in sl]
+    npairs = len(mats) // 2
     iters = max(args.steps // max(args.reps, 1), 1)
-    t_single = per_launch(lambda i: qmv.qmv_q4_0(slots[i % S][0], xd, y1, N, K, 1), iters)
-    t_pair = per_launch(lambda i: qmv.qmv_q4_0_geglu(slots[i % S][1], slots[i % S][2], xd, h, N, K, 1), iters)
+    t_single = per_launch(lambda i: qmv.qmv_q4_0(mats[i % len(mats)], xd, y1, N, K, 1), iters)
+    t_pair = per_launch(lambda i: qmv.qmv_q4_0_geglu(mats[2 * (i % npairs)], mats[2 * (i % npairs) + 1],
+                                                     xd, h, N, K, 1), iters)
 
     for i in range(args.warmup):
         step(i)
