@@ -270,8 +270,16 @@ int logits_sample(const void* W_q8_0, const float* x, const float* u, int32_t* t
         rc = launched(qmv::launch_gemv(1, W_q8_0, nullptr, x + m * K, nullptr, y + m * N, N, K, stream));
         if (rc) return rc;
     }
-    rc = launched(qmv::launch_topk(y, top_val, top_idx, N, M, k, softcap, ws, stream));
-    if (rc) return rc;
+    // the selection kernel makes the draw too where it can (one launch fewer)
+    qmv::TopPDraw draw;
+    draw.u = u;
+    draw.token = token;
+    draw.nucleus = nucleus;
+    draw.temperature = temperature;
+    draw.top_p = top_p;
+    bool drawn = false;
+    rc = launched(qmv::launch_topk(y, top_val, top_idx, N, M, k, softcap, ws, stream, draw, &drawn));
+    if (rc || drawn) return rc;
     return launched(qmv::launch_sample(top_val, top_idx, u, token, nucleus, M, k, temperature, top_p, stream));
 }
 

@@ -31,10 +31,24 @@ hipError_t launch_gemv_mxfp4(const void* codes, const void* scales, const float*
 hipError_t launch_qkv(const void* Wq, const void* Wk, const void* Wv, const float* x, float* yq, float* yk, float* yv,
                       int64_t Nq, int64_t Nk, int64_t Nv, int64_t K, hipStream_t stream);
 
-// Top-k over y[M][N] (float32), candidates in ws.
+// A top-p draw from the k selected pairs of each row: the caller's uniform
+// numbers u[M], the drawn token and nucleus size per row.  token == nullptr:
+// no draw.
+struct TopPDraw {
+    const float* u = nullptr;
+    int32_t* token = nullptr;
+    int32_t* nucleus = nullptr;
+    float temperature = 1.0f;
+    float top_p = 1.0f;
+};
+
+// Top-k over y[M][N] (float32), candidates in ws.  With draw.token set, the
+// selection kernel also makes the draw when its path allows (*drawn = true);
+// otherwise launch_sample must follow.
 size_t topk_ws_bytes(int64_t N, int64_t M, int k);
 hipError_t launch_topk(const float* y, float* top_val, int32_t* top_idx, int64_t N, int64_t M,
-                       int k, float softcap, void* ws, hipStream_t stream);
+                       int k, float softcap, void* ws, hipStream_t stream, const TopPDraw& draw = TopPDraw{},
+                       bool* drawn = nullptr);
 
 // The workspace of logits_topk_noalloc: a device array of this many bytes,
 // one per GPU, never allocated or freed by a call.  static_scratch() gives

@@ -278,11 +278,49 @@ void topk_chunk_kernel(const float* __restrict__ y, int64_t N, int k, int nwchun
     }
 }
 
+// The top-p draw of one row by one whole wave, lane i holding the i-th
+// largest capped value z and its index (lanes >= k: have = false)
+// ["Gemma 4 M4 Max kernel roadmap", K5: top-k40 / top-p token selection on
+// the device after the tied projection]:
+//   w_i = exp((z_i - z_0) / T) for i < k (z sorted, largest first; NaN -> 0),
+//   n   = the smallest count whose prefix sum reaches top_p * sum(w)  (n >= 1),
+//   j   = the first i < n whose prefix sum exceeds u * (prefix sum of n),
+//   token = index_j.
+// The prefix sums are one inclusive wave scan (a fixed order, so the draw is
+// reproducible).
+__device__ void draw_topp(float z, int32_t idx, bool have, int64_t m, int k, const TopPDraw& D) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const float z0 = __shfl(z, 0, kWave);
+    float w = 0.0f;
+    if (have && z == z && z0 == z0) w = expf((z - z0) / D.temperature);
+    float cum = w;
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+        const float t = __shfl_up(cum, o, kWave);
+        if (lane >= o) cum += t;
+    }
+    const float total = __shfl(cum, kWave - 1, kWave);
+    int n = 1, j = 0;
+    if (total > 0.0f) {
+        const uint64_t reach = __ballot(have && cum >= D.top_p * total);
+        n = reach ? __ffsll(static_cast<unsigned long long>(reach)) : k;  // first lane reaching, plus one
+        const float cut = __shfl(cum, n - 1, kWave);
+        const float target = D.u[m] * cut;
+        const uint64_t past = __ballot(lane < n && cum > target);
+        j = past ? __ffsll(static_cast<unsigned long long>(past)) - 1 : n - 1;
+    }
+    const int32_t tok = __shfl(idx, j, kWave);
+    if (lane == 0) {
+        D.token[m] = tok;
+        D.nucleus[m] = n;
+    }
+}
+
 // Tournament over nlists <= 1024 sorted lists of k keys.
 __global__ __launch_bounds__(kMergeThreads)
 void topk_tournament_kernel(const float* __restrict__ y, int64_t N, int k, int nlists, float softcap,
                             const uint64_t* __restrict__ cand, float* __restrict__ top_val,
-                            int32_t* __restrict__ top_idx) {
+                            int32_t* __restrict__ top_idx, TopPDraw draw) {
     // Level 1: every wave runs its own tournament over its 64 lists (a wave
     // maximum per round, no workgroup barrier) and keeps its k winners in
     // LDS.  Level 2: wave 0 runs the tournament over the 16 waves' lists.
@@ -327,6 +365,8 @@ void topk_tournament_kernel(const float* __restrict__ y, int64_t N, int k, int n
             head = pos < k ? wlist[lane][pos] : 0ull;
         }
     }
+    float z = 0.0f;
+    int32_t zi = -1;
     if (lane < k) {
         // k <= N guarantees a real key every round; a zero key would mean
         // "nothing left" and is never dereferenced.
@@ -334,9 +374,12 @@ void topk_tournament_kernel(const float* __restrict__ y, int64_t N, int k, int n
         const uint32_t idx = 0xFFFFFFFFu - static_cast<uint32_t>(g);
         const bool real = g != 0ull && idx < static_cast<uint64_t>(N);
         const float v = real ? y[static_cast<int64_t>(m) * N + idx] : __builtin_nanf("");
-        top_idx[static_cast<int64_t>(m) * k + lane] = real ? static_cast<int32_t>(idx) : -1;
-        top_val[static_cast<int64_t>(m) * k + lane] = softcap * tanhf(v / softcap);
+        zi = real ? static_cast<int32_t>(idx) : -1;
+        z = softcap * tanhf(v / softcap);
+        top_idx[static_cast<int64_t>(m) * k + lane] = zi;
+        top_val[static_cast<int64_t>(m) * k + lane] = z;
     }
+    if (draw.token) draw_topp(z, zi, lane < k, m, k, draw);
 }
 
 // Stage 2 over nlists <= 1024 sorted lists of k keys (chunk: entries per
@@ -344,7 +387,7 @@ void topk_tournament_kernel(const float* __restrict__ y, int64_t N, int k, int n
 __global__ __launch_bounds__(kMergeThreads)
 void topk_select_kernel(const float* __restrict__ y, int64_t N, int k, int nlists, int chunk, float softcap,
                         const uint64_t* __restrict__ cand, float* __restrict__ top_val,
-                        int32_t* __restrict__ top_idx) {
+                        int32_t* __restrict__ top_idx, TopPDraw draw) {
     __shared__ uint64_t lds[2 * kMaxCand];  // sort buffers, then the candidates
     __shared__ uint64_t sh_T;
     __shared__ int sh_off[kWave + 1];
@@ -430,14 +473,21 @@ void topk_select_kernel(const float* __restrict__ y, int64_t N, int k, int nlist
         block_sort_desc(key, lds);
         best = key[0];
     }
-    if (t < k) {
-        // k <= N guarantees a real key at every rank < k; a zero key would
-        // mean "nothing left" and is never dereferenced.
-        const uint32_t idx = 0xFFFFFFFFu - static_cast<uint32_t>(best);
-        const bool real = best != 0ull && idx < static_cast<uint64_t>(N);
-        const float v = real ? y[static_cast<int64_t>(m) * N + idx] : __builtin_nanf("");
-        top_idx[static_cast<int64_t>(m) * k + t] = real ? static_cast<int32_t>(idx) : -1;
-        top_val[static_cast<int64_t>(m) * k + t] = softcap * tanhf(v / softcap);
+    if (t < kWave) {  // wave 0; k <= 64
+        float z = 0.0f;
+        int32_t zi = -1;
+        if (t < k) {
+            // k <= N guarantees a real key at every rank < k; a zero key would
+            // mean "nothing left" and is never dereferenced.
+            const uint32_t idx = 0xFFFFFFFFu - static_cast<uint32_t>(best);
+            const bool real = best != 0ull && idx < static_cast<uint64_t>(N);
+            const float v = real ? y[static_cast<int64_t>(m) * N + idx] : __builtin_nanf("");
+            zi = real ? static_cast<int32_t>(idx) : -1;
+            z = softcap * tanhf(v / softcap);
+            top_idx[static_cast<int64_t>(m) * k + t] = zi;
+            top_val[static_cast<int64_t>(m) * k + t] = z;
+        }
+        if (draw.token) draw_topp(z, zi, t < k, m, k, draw);
     }
 }
 
@@ -503,46 +553,18 @@ int64_t wave_chunks_of(int64_t N) {
 size_t align256(size_t b) { return (b + 255) & ~static_cast<size_t>(255); }
 
 // ---------------------------------------------------------- sampling
-// One wave per row draws a token from the k selected (value, index) pairs
-// ["Gemma 4 M4 Max kernel roadmap", K5: top-k40 / top-p token selection on
-// the device after the tied projection]:
-//   w_i = exp((z_i - z_0) / T) for i < k (z sorted, largest first; NaN -> 0),
-//   n   = the smallest count whose prefix sum reaches top_p * sum(w)  (n >= 1),
-//   j   = the first i < n whose prefix sum exceeds u * (prefix sum of n),
-//   token = index_j.
-// Lane i holds candidate i; the prefix sums are one inclusive wave scan (a
-// fixed order, so the draw is reproducible).
+// The draw of draw_topp from k given pairs per row (one wave per row): the
+// path of logits_sample when the selection kernel cannot make it, and the
+// test export.
 __global__ __launch_bounds__(kWave)
-void sample_topp_kernel(const float* __restrict__ top_val, const int32_t* __restrict__ top_idx,
-                        const float* __restrict__ u, int32_t* __restrict__ token, int32_t* __restrict__ nucleus,
-                        int k, float temperature, float top_p) {
+void sample_topp_kernel(const float* __restrict__ top_val, const int32_t* __restrict__ top_idx, int k,
+                        TopPDraw draw) {
     const int64_t m = blockIdx.x;
     const int lane = threadIdx.x;
     const bool have = lane < k;
     const float z = have ? top_val[m * k + lane] : 0.0f;
-    const float z0 = __shfl(z, 0, kWave);
-    float w = 0.0f;
-    if (have && z == z && z0 == z0) w = expf((z - z0) / temperature);
-    float cum = w;
-#pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) {
-        const float t = __shfl_up(cum, o, kWave);
-        if (lane >= o) cum += t;
-    }
-    const float total = __shfl(cum, kWave - 1, kWave);
-    int n = 1, j = 0;
-    if (total > 0.0f) {
-        const uint64_t reach = __ballot(have && cum >= top_p * total);
-        n = reach ? __ffsll(static_cast<unsigned long long>(reach)) : k;  // first lane reaching, plus one
-        const float cut = __shfl(cum, n - 1, kWave);
-        const float target = u[m] * cut;
-        const uint64_t past = __ballot(lane < n && cum > target);
-        j = past ? __ffsll(static_cast<unsigned long long>(past)) - 1 : n - 1;
-    }
-    if (lane == 0) {
-        token[m] = top_idx[m * k + j];
-        nucleus[m] = n;
-    }
+    const int32_t zi = have ? top_idx[m * k + lane] : -1;
+    draw_topp(z, zi, have, m, k, draw);
 }
 
 }  // namespace
@@ -555,7 +577,8 @@ size_t topk_ws_bytes(int64_t N, int64_t M, int k) {
 }
 
 hipError_t launch_topk(const float* y, float* top_val, int32_t* top_idx, int64_t N, int64_t M, int k,
-                       float softcap, void* ws, hipStream_t stream) {
+                       float softcap, void* ws, hipStream_t stream, const TopPDraw& draw, bool* drawn) {
+    if (drawn) *drawn = false;
     const int nwchunks = static_cast<int>(wave_chunks_of(N));
     uint64_t* cand = reinterpret_cast<uint64_t*>(
         static_cast<char*>(ws) + align256(static_cast<size_t>(N) * static_cast<size_t>(M) * sizeof(float)));
@@ -576,10 +599,12 @@ hipError_t launch_topk(const float* y, float* top_val, int32_t* top_idx, int64_t
     if (e != hipSuccess) return e;
     if (nwchunks <= kMaxLists && k > kRoundsMaxK) {
         hipLaunchKernelGGL(topk_select_kernel, dim3(static_cast<unsigned>(M)), dim3(kMergeThreads), 0, stream,
-                           y, N, k, nwchunks, kWave * keys_per_lane(N), softcap, cand, top_val, top_idx);
+                           y, N, k, nwchunks, kWave * keys_per_lane(N), softcap, cand, top_val, top_idx, draw);
+        if (drawn) *drawn = draw.token != nullptr;
     } else if (nwchunks <= kMaxLists) {
         hipLaunchKernelGGL(topk_tournament_kernel, dim3(static_cast<unsigned>(M)), dim3(kMergeThreads), 0, stream,
-                           y, N, k, nwchunks, softcap, cand, top_val, top_idx);
+                           y, N, k, nwchunks, softcap, cand, top_val, top_idx, draw);
+        if (drawn) *drawn = draw.token != nullptr;
     } else {
         hipLaunchKernelGGL(topk_merge_scan_kernel, dim3(static_cast<unsigned>(M)), dim3(kMergeThreads), 0, stream,
                            y, N, k, nwchunks, softcap, cand, top_val, top_idx);
@@ -614,8 +639,14 @@ void* static_scratch() {
 
 hipError_t launch_sample(const float* top_val, const int32_t* top_idx, const float* u, int32_t* token,
                          int32_t* nucleus, int64_t M, int k, float temperature, float top_p, hipStream_t stream) {
-    hipLaunchKernelGGL(sample_topp_kernel, dim3(static_cast<unsigned>(M)), dim3(kWave), 0, stream, top_val, top_idx, u,
-                       token, nucleus, k, temperature, top_p);
+    TopPDraw draw;
+    draw.u = u;
+    draw.token = token;
+    draw.nucleus = nucleus;
+    draw.temperature = temperature;
+    draw.top_p = top_p;
+    hipLaunchKernelGGL(sample_topp_kernel, dim3(static_cast<unsigned>(M)), dim3(kWave), 0, stream, top_val, top_idx, k,
+                       draw);
     return hipGetLastError();
 }
 

@@ -27,7 +27,9 @@ hipError_t launch_gemv_mxfp4(const void*, const void*, const float*, float*, int
 hipError_t launch_qkv(const void*, const void*, const void*, const float*, float*, float*, float*, int64_t Nq,
                       int64_t, int64_t, int64_t K, hipStream_t) { rec(Nq, K); return hipSuccess; }
 size_t topk_ws_bytes(int64_t N, int64_t M, int k) { return static_cast<size_t>(N * M * 4 + M * k * 8 * 64); }
-hipError_t launch_topk(const float*, float*, int32_t*, int64_t N, int64_t, int, float, void*, hipStream_t) {
+hipError_t launch_topk(const float*, float*, int32_t*, int64_t N, int64_t, int, float, void*, hipStream_t,
+                       const TopPDraw&, bool* drawn) {
+    if (drawn) *drawn = false;  // so that logits_sample also reaches launch_sample
     rec(N, 0); return hipSuccess; }
 void* static_scratch() { alignas(256) static unsigned char buf[4096]; return buf; }
 hipError_t launch_sample(const float*, const int32_t*, const float*, int32_t*, int32_t*, int64_t M, int k, float,

@@ -105,3 +105,34 @@ def test_logits_sample(K):
     for m in range(M):
         check_selection(idx[m], vals[m], y[m], yr[m], S[m], k, cap, f"K={K} row {m}")
     check_draw(vals, idx, u, host(tok), host(nuc), T, p, f"logits_sample K={K}")
+
+
+@pytest.mark.parametrize("N,K,k", [(262144, 64, 1), (262144, 64, 10), (262144, 64, 16), (262144, 64, 17),
+                                   (262144, 64, 64), (100003, 96, 40), (4 * 1024 * 1024 + 1, 32, 10)])
+def test_logits_sample_paths(N, K, k):
+    """Every selection path of logits_sample: the rounds and tournament
+    (k <= 16) and the sorted threshold selection (k > 16) make the draw in the
+    selection kernel itself; past 4M logits the scan merge is followed by the
+    separate draw kernel.  The draw must equal, bit for bit, what the draw
+    export makes from the selected pairs, and pass the oracle's check."""
+    qmv = _qmv()
+    M, cap, T, p = 3, 30.0, 0.8, 0.9
+    W = synth.q8_0_weights(N, K, 500 + k)
+    x = synth.activations(M, K, 501 + k)
+    u = np.array([0.05, 0.5, 0.95], dtype=np.float32)
+    say(f"logits_sample paths N={N} K={K} M={M} k={k}")
+    wsb = qmv.logits_topk_ws_bytes(N, M, k)
+    ws = torch.empty(wsb, dtype=torch.uint8, device="cuda:0")
+    vals, idx = empty((M, k)), empty((M, k), dtype=torch.int32)
+    tok, nuc = empty((M,), dtype=torch.int32), empty((M,), dtype=torch.int32)
+    ud = dev(u)
+    qmv.logits_sample(dev(W), dev(x), ud, tok, nuc, vals, idx, N, K, M, k, cap, T, p, ws, wsb)
+    tok2, nuc2 = empty((M,), dtype=torch.int32), empty((M,), dtype=torch.int32)
+    qmv.qmvdbg_sample_f32(vals, idx, ud, tok2, nuc2, M, k, T, p)
+    assert np.array_equal(host(tok), host(tok2)) and np.array_equal(host(nuc), host(nuc2))
+    y = host(ws[: M * N * 4].view(torch.float32).reshape(M, N))
+    vals, idx = host(vals), host(idx)
+    yr, S = oracle.qmv("q8_0", W, N, K, x, M=M)
+    for m in range(M):
+        check_selection(idx[m], vals[m], y[m], yr[m], S[m], k, cap, f"N={N} k={k} row {m}")
+    check_draw(vals, idx, u, host(tok), host(nuc), T, p, f"logits_sample N={N} k={k}")
