@@ -74,7 +74,11 @@ def profiled_traffic(kernel: str, grid: int):
     return None
 
 
-TRACE_PROFILE = os.path.join("profiles", "qmv_bench_workloads_kernel_trace.md")
+# Kernel-trace means of the two timed launches come from a trace of the
+# headline loops alone (bench.py --no-rows): in the full run other rows launch
+# the same kernels at the same grid on other data (e.g. eight rows over one
+# matrix), which would mix into the mean.
+TRACE_PROFILE = os.path.join("profiles", "qmv_bench_headline_kernel_trace.md")
 
 
 def _sources_match(text):
@@ -663,7 +667,7 @@ def trace_summary(directory: str, command: str) -> str:
     for r in _csv_rows(directory, "kernel_trace.csv"):
         key = (_kernel_symbol(r["Kernel_Name"]), _workgroups(r))
         groups.setdefault(key, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1000.0)
-    lines = ["# Kernel trace of bench.py: every kernel the benchmark launches", "",
+    lines = ["# Kernel trace of bench.py: every kernel the command below launches", "",
              "Command (from the repository root, one MI355X):", "", "```", command, "```", "",
              "Durations from the kernel trace, per kernel symbol and grid (workgroups):", "",
              "| kernel | grid | calls | mean us | median us | min us | max us |", "|---|---|---|---|---|---|---|"]
