@@ -478,9 +478,9 @@ def measure_rows(torch, qmv, synth, dev):
         xd, y = t(x), torch.empty((M, N), device=dev)
         wsb = qmv.qmm_q4_0_q8act_ws_bytes(N, K, M)
         ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
-        iters = 100 if M < 512 else 5
+        iters = 100 if M < 512 else 20
         ms = _time_loop(torch, lambda i: qmv.qmm_q4_0_q8act(slots[i % 8], xd, y, N, K, M, ws, wsb), iters,
-                        warm=2)
+                        warm=2 if M < 512 else 10)
         b = W.nbytes + M * K * 4 + M * N * 4
         res[f"c4_qmm_q4_0_q8act_M{M}"] = {"us": ms * 1e3, "bytes": b, "GB/s": b / ms / 1e6,
                                           "int_TOPS": 2.0 * M * N * K / ms / 1e9}
