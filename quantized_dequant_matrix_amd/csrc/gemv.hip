@@ -615,12 +615,16 @@ void gemv_split_kernel(const uint8_t* __restrict__ W, const uint8_t* __restrict_
     int c0 = g0;
     int cn = min(CH, g1 - c0);
     int slot = wave;
+    // The activations are staged before the first slot's weights are
+    // requested, so that the staging's wait (loads complete in issue order for
+    // the wait counter) does not include the weights and the decode starts as
+    // they arrive: 2-5% faster for every format at the down shape.
     bool have = false;  // U holds the weights of (c0, slot)
+    stage_x<GIN>(xs, x, xu, G, blockDim.x);
     if (slot < cn * KS) {
         load(c0, slot);
         have = true;
     }
-    stage_x<GIN>(xs, x, xu, G, blockDim.x);
     __syncthreads();
 
     while (c0 < g1) {
