@@ -254,3 +254,38 @@ def test_qmm_integer_valued_is_exact(N, K, M):
     y = gpu_qmm(W, x, N, K, M)
     yr, _ = _qmm_ref(W, x, N, K, M)
     assert np.array_equal(y, yr)
+
+
+def _draw_qmm(rng):
+    """(N, K, M) for the int8 MFMA tilings: half of the draws take the wide
+    one (at least 512 tiles of 64 x 64, with and without the shared last
+    tiles), half the narrow one; N and M on and off the tile edges, K a whole
+    number of 256-element units with an odd or even count of 16-block chunks."""
+    K = 256 * int(rng.integers(1, 24))
+    if rng.integers(0, 2):
+        M = int(rng.integers(257, 700))
+        tiles_m = -(-M // 64)
+        N = 64 * int(rng.integers(-(-512 // tiles_m), 767 // tiles_m + 1)) - int(rng.integers(0, 64))
+    else:
+        M = int(rng.integers(2, 200))
+        N = int(rng.integers(16, 3000))
+    return N, K, M
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_qmm_random(seed):
+    """Seeded random shapes through qmm_q4_0_q8act: the block sums of a row
+    range across tile edges bit for bit, and y on sampled rows within the
+    tolerance."""
+    rng = np.random.default_rng(4000 + seed)
+    N, K, M = _draw_qmm(rng)
+    path = qmm_path(N, K, M)
+    n0 = int(rng.integers(0, max(1, N - 200)))
+    n1 = min(N, n0 + 200)
+    say(f"random qmm_q4_0_q8act N={N} K={K} M={M} ({path}) rows {n0}..{n1} seed={seed}")
+    W, x = synth.problem("q4_0", N, K, M, 500 + seed)
+    assert np.array_equal(gpu_blocksums(W, x, N, K, M, n0, n1), ref_blocksums(W, x, N, K, M, n0, n1))
+    y = gpu_qmm(W, x, N, K, M)
+    rows = np.unique(np.concatenate([[0, N - 1, n0, n1 - 1], rng.choice(N, min(N, 24), replace=False)]))
+    yr, S = _qmm_ref(W, x, N, K, M, rows=rows)
+    assert_within(y[:, rows], yr, oracle.float_tol(S), f"random qmm {N}x{K} M={M}")
