@@ -680,7 +680,9 @@ void qmm_wide_kernel(const uint8_t* __restrict__ W, const int8_t* __restrict__ x
         share = xcd_run(item - S.whole, S.parts);
         const int64_t u0 = share_start(share, S), u1 = share_start(share + 1, S);
         nseg = 0;
-        for (int64_t u = u0; u < u1;) {
+        // a share is shorter than a tile (the plan splits fewer than 256
+        // tiles over 256 shares), so it meets at most two of them
+        for (int64_t u = u0; u < u1 && nseg < 2;) {
             const int64_t r = u / S.nch;  // remaining tile
             const int64_t ue = ((r + 1) * S.nch < u1) ? (r + 1) * S.nch : u1;
             seg_tile[nseg] = S.whole + r;
