@@ -309,6 +309,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "prewarm_ms": args.prewarm_ms,
         "ms_per_step": round(ms_step, 5),
         "ms_per_step_windows": [round(w, 5) for w in windows],
         "window_spread": round(_spread(windows), 4),
